@@ -1,0 +1,169 @@
+/*
+ * libmiattn: fused exact attention for AMD Instinct MI355X (gfx950).
+ *
+ * Computes O = softmax(mod(scale * Q K^T) masked) V tile by tile with an
+ * online softmax (running row max, running normaliser, rescaled output
+ * accumulator), so the Sq x Skv score matrix never reaches device memory.
+ *
+ * Sources for what is computed (web pages, cited by title and section):
+ *  - "FlashAttention 설명" (FlashAttention explainer), §1: the definition
+ *    softmax(QK^T/sqrt(d))V; §3-§6: never materialise the score matrix,
+ *    online softmax with running max / normaliser / output, tiling through
+ *    on-chip memory, result identical to the plain definition.
+ *  - "FlashAttention-2 — GPU attention의 사실상 표준", §3-§4: Q row tiles,
+ *    K/V column tiles, backward pass recomputes the scores.
+ *  - "PyTorch FlexAttention, FlashAttention-4 백엔드 도입" (섹션별 상세):
+ *    score modifiers receive (score, batch, head, q_idx, kv_idx); ALiBi,
+ *    sliding window, document masking, tanh soft-cap, local boost; block-
+ *    sparse iteration skips fully masked blocks; 128x128 mask blocks.
+ *  - "FlashInfer SM120 NVFP4 어텐션 최적화" §1-§2: separate query/output
+ *    and key/value head counts, optional LSE output [B, Hq, S] float32.
+ *
+ * Conventions (all entry points):
+ *  - Layout: Q, O [B][Hq][Sq][D]; K, V [B][Hkv][Skv][D]; contiguous, D
+ *    innermost.  LSE [B][Hq][Sq] float32, natural-log units.  Device
+ *    pointers must be 16-byte aligned.
+ *  - Ownership: the caller owns every buffer.  The library allocates no
+ *    device memory, keeps no mutable global state, and is re-entrant.
+ *    Parameter structs are host memory read during the call only; the
+ *    arrays they point to (doc_ids, alibi_slopes, block-mask arrays) are
+ *    device memory.
+ *  - Errors: an fa_status is returned.  All argument validation happens
+ *    before any HIP call, so an invalid call has no device side effect.
+ *    A failed launch maps to FA_ERR_LAUNCH.  Nothing is thrown or aborted.
+ *  - Execution is asynchronous on `stream` (a hipStream_t; NULL = the
+ *    default stream).  The library never synchronises.
+ *  - GQA / MQA: G = Hq / Hkv; query head h uses key/value head h / G.
+ *  - Indices in masks and modifiers are absolute (query i in [0,Sq), key j
+ *    in [0,Skv)); causal means j <= i even when Sq != Skv.
+ */
+#ifndef LIBMIATTN_H
+#define LIBMIATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,        /* a required pointer is NULL */
+  FA_ERR_SHAPE = -2,       /* sizes negative, inconsistent or too large */
+  FA_ERR_UNSUPPORTED = -3, /* head dim / dtype / combination not built */
+  FA_ERR_ALIGN = -4,       /* a device pointer is not 16-byte aligned */
+  FA_ERR_PARAM = -5,       /* mask or modifier parameter out of range */
+  FA_ERR_WORKSPACE = -6,   /* workspace missing or too small */
+  FA_ERR_LAUNCH = -7       /* the kernel launch failed */
+} fa_status;
+
+typedef enum { FA_BF16 = 0, FA_F32 = 1 } fa_dtype;
+
+/* Masks ("PyTorch FlexAttention, FlashAttention-4" page, 섹션별 상세 and
+ * 핵심 요약: sliding window and document masking as mask_mod examples). */
+typedef enum {
+  FA_MASK_NONE = 0,           /* every key */
+  FA_MASK_CAUSAL = 1,         /* j <= i */
+  FA_MASK_SLIDING_WINDOW = 2, /* j <= i and i - j < window */
+  FA_MASK_DOCUMENT = 3        /* doc_ids[b][i] == doc_ids[b][j] and j <= i */
+} fa_mask_kind;
+
+/* Score modifiers, applied to the scaled score s = scale * q_i . k_j (same
+ * page: score_mod(score, b, h, q_idx, kv_idx); the soft-cap and local_boost
+ * code examples; ALiBi named in the summary). */
+typedef enum {
+  FA_MOD_NONE = 0,
+  FA_MOD_ALIBI = 1,       /* s + slope[h] * (j - i) */
+  FA_MOD_SOFTCAP = 2,     /* softcap * tanh(s / softcap) */
+  FA_MOD_LOCAL_BOOST = 3  /* |i - j| < boost_radius ? s * boost_factor : s */
+} fa_mod_kind;
+
+typedef struct {
+  int32_t window;          /* FA_MASK_SLIDING_WINDOW: keys per query, >= 1 */
+  const int32_t* doc_ids;  /* FA_MASK_DOCUMENT: device int32 [B][S] */
+  int32_t* visited;        /* optional debug output, device int32
+                              [B][Hq][ceil(Sq/128)]: fa_fwd ADDS the number of
+                              key steps (of fa_fwd_kv_step() columns) each
+                              128-row query tile processed.  NULL in production. */
+} fa_mask_params;
+
+typedef struct {
+  const float* alibi_slopes; /* device float [Hq]; NULL: 2^(-8(h+1)/Hq) */
+  float softcap;             /* FA_MOD_SOFTCAP: > 0 */
+  int32_t boost_radius;      /* FA_MOD_LOCAL_BOOST: >= 0 */
+  float boost_factor;        /* FA_MOD_LOCAL_BOOST: finite */
+} fa_mod_params;
+
+/* Tile states of a block mask. */
+enum { FA_TILE_EMPTY = 0, FA_TILE_PARTIAL = 1, FA_TILE_FULL = 2 };
+
+/* Block mask at block_q x block_kv granularity ("PyTorch FlexAttention,
+ * FlashAttention-4" page, 섹션별 상세: block-sparse iteration skips masked
+ * blocks; 128x128 blocks).  A tile is EMPTY when no in-range pair is
+ * admissible, FULL when every pair is in range and admissible, PARTIAL
+ * otherwise.  The arrays are device memory owned by the caller.
+ * n_b is 1 (one mask for every batch row) or B (document masks). */
+typedef struct {
+  int32_t block_q, block_kv; /* must both be 128 */
+  int32_t n_q, n_kv;         /* ceil(Sq/block_q), ceil(Skv/block_kv) */
+  int32_t n_b;               /* 1 or B */
+  uint8_t* tile_state;       /* [n_b][n_q][n_kv] FA_TILE_* */
+  int32_t* kv_count;         /* [n_b][n_q]  non-empty kv tiles per q tile */
+  int32_t* kv_index;         /* [n_b][n_q][n_kv] ascending, first kv_count valid */
+  int32_t* q_count;          /* [n_b][n_kv] non-empty q tiles per kv tile */
+  int32_t* q_index;          /* [n_b][n_kv][n_q] ascending, first q_count valid */
+} fa_block_mask;
+
+/* Forward pass.  q, k, v, out: device, dtype elements in the layout above.
+ * lse: device float [B][Hq][Sq] or NULL (no LSE written).  scale multiplies
+ * q . k before the modifier.  mask_params / mod_params: host structs, may be
+ * NULL when the kind needs no parameter.  block_mask: NULL (tile ranges
+ * derived from the mask kind) or a mask built for this (mask, B, Sq, Skv);
+ * when given, only its non-empty tiles are visited and FULL tiles skip the
+ * elementwise mask.  Rows with no admissible key get O = 0, LSE = -inf.
+ * B == 0 or Sq == 0 is a valid no-op.  Supported: D in {64, 128}; dtype
+ * FA_BF16 or FA_F32 (fp32 inputs/outputs, fp32 products). */
+int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+           int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype, float scale,
+           int mask_kind, const fa_mask_params* mask_params,
+           int score_mod_kind, const fa_mod_params* mod_params,
+           const fa_block_mask* block_mask, void* stream);
+
+/* Width in keys of one forward key step (the unit of fa_mask_params.visited). */
+int fa_fwd_kv_step(int D, int dtype);
+
+/* Backward pass with recomputation ("FlashAttention-2" page §3-§4: the
+ * backward pass recomputes the scores instead of storing them).  Given the
+ * forward's out and lse (lse is required) and dout, writes dq [B][Hq][Sq][D]
+ * and dk, dv [B][Hkv][Skv][D] (summed over each GQA group), accumulating in
+ * float32 and rounding once.  workspace: device, at least
+ * fa_bwd_workspace_bytes(B, Hq, Sq, D) bytes, 16-byte aligned, contents
+ * need not be initialised.  Supported: dtype FA_BF16, D in {64, 128}, every
+ * mask and modifier. */
+int fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+           int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype, float scale,
+           int mask_kind, const fa_mask_params* mask_params,
+           int score_mod_kind, const fa_mod_params* mod_params,
+           const fa_block_mask* block_mask, void* stream);
+
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq, int D);
+
+/* Build a block mask for (mask_kind, mask_params, B, Sq, Skv) into the
+ * caller's arrays described by *out (block sizes, n_q, n_kv, n_b and the five
+ * pointers must be set; n_b must be B for FA_MASK_DOCUMENT and may be 1
+ * otherwise).  One stream-ordered pass; every entry of every array is
+ * written (unused list slots are set to -1). */
+int fa_block_mask_build(int mask_kind, const fa_mask_params* mask_params,
+                        int B, int Sq, int Skv, const fa_block_mask* out, void* stream);
+
+const char* fa_status_str(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBMIATTN_H */

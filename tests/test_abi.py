@@ -1,0 +1,141 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, and rejects invalid arguments before touching the GPU (CPU only;
+no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import tiled_attention_fa_amd as fa
+from tiled_attention_fa_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libmiattn.h")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not os.path.exists(binding.LIB_PATH):
+        from tiled_attention_fa_amd import build
+        build.build()
+    return fa.lib()
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared() == sorted(binding.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for name in declared():
+        assert name in syms, name
+        assert hasattr(fa.lib(), name)
+
+
+def test_host_helpers():
+    assert fa.fa_version() == 100
+    assert fa.fa_status_str(0) == "ok"
+    assert "workspace" in fa.fa_status_str(fa.FA_ERR_WORKSPACE)
+    assert fa.fa_fwd_kv_step(128, fa.FA_BF16) == 64
+    assert fa.fa_fwd_kv_step(64, fa.FA_F32) == 32
+    assert fa.fa_fwd_kv_step(96, fa.FA_BF16) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd_workspace_bytes(2, 16, 8192, 128) == 2 * 16 * 8192 * 4
+    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 64) == 256
+
+
+P = ctypes.c_void_p(0x100000)      # never dereferenced: every call below fails validation
+MIS = ctypes.c_void_p(0x100008)    # not 16-byte aligned
+
+
+def fwd(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=2, Hkv=2, Sq=16, Skv=16, D=64, dtype=0, scale=0.125,
+        mask=0, mp=None, mod=0, op=None, bm=None):
+    return fa.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, dtype, scale, mask,
+                     ctypes.byref(mp) if mp else None, mod, ctypes.byref(op) if op else None,
+                     ctypes.byref(bm) if bm else None, None)
+
+
+def test_fwd_rejects_bad_shapes():
+    assert fwd(D=96) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(dtype=7) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(Hq=3, Hkv=2) == fa.FA_ERR_SHAPE
+    assert fwd(B=-1) == fa.FA_ERR_SHAPE
+    assert fwd(Sq=-5) == fa.FA_ERR_SHAPE
+    assert fwd(Hkv=0) == fa.FA_ERR_SHAPE
+    assert fwd(Sq=1 << 23) == fa.FA_ERR_SHAPE
+
+
+def test_fwd_rejects_bad_pointers():
+    assert fwd(q=None) == fa.FA_ERR_NULL
+    assert fwd(o=None) == fa.FA_ERR_NULL
+    assert fwd(k=None) == fa.FA_ERR_NULL
+    assert fwd(q=MIS) == fa.FA_ERR_ALIGN
+    assert fwd(v=MIS) == fa.FA_ERR_ALIGN
+    assert fwd(lse=ctypes.c_void_p(0x100002)) == fa.FA_ERR_ALIGN
+
+
+def test_fwd_rejects_bad_params():
+    assert fwd(scale=-1.0) == fa.FA_ERR_PARAM
+    assert fwd(scale=float("nan")) == fa.FA_ERR_PARAM
+    assert fwd(mask=2) == fa.FA_ERR_NULL
+    assert fwd(mask=2, mp=fa.FaMaskParams(0, None, None)) == fa.FA_ERR_PARAM
+    assert fwd(mask=3, mp=fa.FaMaskParams(0, None, None)) == fa.FA_ERR_NULL
+    assert fwd(mask=3, mp=fa.FaMaskParams(0, 0x200000, None), Skv=32) == fa.FA_ERR_SHAPE
+    assert fwd(mask=9) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(mod=2) == fa.FA_ERR_NULL
+    assert fwd(mod=2, op=fa.FaModParams(None, 0.0, 0, 1.0)) == fa.FA_ERR_PARAM
+    assert fwd(mod=2, op=fa.FaModParams(None, float("inf"), 0, 1.0)) == fa.FA_ERR_PARAM
+    assert fwd(mod=3, op=fa.FaModParams(None, 0.0, -1, 1.1)) == fa.FA_ERR_PARAM
+    assert fwd(mod=3, op=fa.FaModParams(None, 0.0, 5, float("nan"))) == fa.FA_ERR_PARAM
+    assert fwd(mod=8) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_fwd_rejects_bad_block_mask():
+    good = dict(block_q=128, block_kv=128, n_q=1, n_kv=1, n_b=1, tile_state=0x300000, kv_count=0x300100,
+                kv_index=0x300200, q_count=0x300300, q_index=0x300400)
+    assert fwd(bm=fa.FaBlockMask(**{**good, "block_q": 64})) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(bm=fa.FaBlockMask(**{**good, "n_q": 2})) == fa.FA_ERR_SHAPE
+    assert fwd(bm=fa.FaBlockMask(**{**good, "n_b": 3})) == fa.FA_ERR_SHAPE
+    assert fwd(bm=fa.FaBlockMask(**{**good, "kv_index": None})) == fa.FA_ERR_NULL
+    assert fwd(bm=fa.FaBlockMask(**{**good, "kv_count": 0x300102})) == fa.FA_ERR_ALIGN
+
+
+def test_fwd_empty_batch_is_noop():
+    assert fwd(B=0, q=None, k=None, v=None, o=None) == fa.FA_OK
+    assert fwd(Sq=0, q=None, o=None) == fa.FA_OK
+
+
+def bwd(dtype=0, lse=P, ws=P, ws_bytes=1 << 20, dq=P, B=1, Hq=2, Hkv=2, S=16, D=64):
+    return fa.fa_bwd(P, P, P, P, P, lse, dq, P, P, ws, ws_bytes, B, Hq, Hkv, S, S, D, dtype, 0.125,
+                     0, None, 0, None, None, None)
+
+
+def test_bwd_validation():
+    assert bwd(dtype=1) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(lse=None) == fa.FA_ERR_NULL
+    assert bwd(ws=None) == fa.FA_ERR_WORKSPACE
+    assert bwd(ws_bytes=100) == fa.FA_ERR_WORKSPACE
+    assert bwd(ws=MIS) == fa.FA_ERR_ALIGN
+    assert bwd(dq=MIS) == fa.FA_ERR_ALIGN
+    assert bwd(D=80) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(B=0) == fa.FA_OK
+
+
+def test_block_mask_build_validation():
+    bm = fa.FaBlockMask(128, 128, 1, 1, 1, 0x300000, 0x300100, 0x300200, 0x300300, 0x300400)
+    mp = fa.FaMaskParams(0, 0x200000, None)
+    assert fa.fa_block_mask_build(3, ctypes.byref(mp), 2, 100, 100, ctypes.byref(bm), None) == fa.FA_ERR_SHAPE
+    assert fa.fa_block_mask_build(1, None, 1, 100, 100, None, None) == fa.FA_ERR_NULL
+    assert fa.fa_block_mask_build(1, None, 0, 100, 100, ctypes.byref(bm), None) == fa.FA_ERR_SHAPE
+    bad = fa.FaBlockMask(128, 128, 2, 1, 1, 0x300000, 0x300100, 0x300200, 0x300300, 0x300400)
+    assert fa.fa_block_mask_build(1, None, 1, 100, 100, ctypes.byref(bad), None) == fa.FA_ERR_SHAPE
+    no_q = fa.FaBlockMask(128, 128, 1, 1, 1, 0x300000, 0x300100, 0x300200, None, None)
+    assert fa.fa_block_mask_build(1, None, 1, 100, 100, ctypes.byref(no_q), None) == fa.FA_ERR_NULL

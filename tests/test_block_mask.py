@@ -1,0 +1,92 @@
+"""Block-mask builder and tile skipping: bit-exact against brute force."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import tiled_attention_fa_amd as fa
+from tests.gpu_util import dev
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    (dict(mask=0), 1, 300, 300),
+    (dict(mask=0), 1, 256, 640),
+    (dict(mask=1), 1, 1000, 1000),
+    (dict(mask=1), 1, 200, 700),
+    (dict(mask=2, window=128), 1, 900, 900),
+    (dict(mask=2, window=300), 1, 777, 777),
+    (dict(mask=2, window=1), 1, 513, 513),
+    (dict(mask=3), 2, 1500, 1500),
+    (dict(mask=3), 1, 4096, 4096),
+]
+
+
+def _docs(B, S, seed, lo=1, hi=None):
+    hi = hi or max(2, S // 4)
+    return torch.from_numpy(np.stack([synth.doc_ids_from_lengths(synth.doc_lengths(S, lo, hi, seed + b))
+                                      for b in range(B)])).to(torch.int32)
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_builder_matches_brute_force(case):
+    spec, B, Sq, Skv = CASES[case]
+    doc = _docs(B, Sq, 40 + case) if spec["mask"] == 3 else None
+    bm = fa.build_block_mask(spec["mask"], B, Sq, Skv, window=spec.get("window", 0), doc_ids=dev(doc))
+    torch.cuda.synchronize()
+    var = oracle.Variant(doc_ids=None if doc is None else doc.numpy(), **spec)
+    st, kvl, ql = oracle.tile_states(var, B, Sq, Skv, 128, 128)
+    assert np.array_equal(bm.tile_state.cpu().numpy(), st)
+    kc, ki = bm.kv_count.cpu().numpy(), bm.kv_index.cpu().numpy()
+    qc, qi = bm.q_count.cpu().numpy(), bm.q_index.cpu().numpy()
+    for b in range(st.shape[0]):
+        for t in range(st.shape[1]):
+            n = len(kvl[b][t])
+            assert kc[b, t] == n and np.array_equal(ki[b, t, :n], kvl[b][t]) and np.all(ki[b, t, n:] == -1)
+        for t in range(st.shape[2]):
+            n = len(ql[b][t])
+            assert qc[b, t] == n and np.array_equal(qi[b, t, :n], ql[b][t]) and np.all(qi[b, t, n:st.shape[1]] == -1)
+
+
+def test_doc_config_shape_mask():
+    """The packed-document workload's mask (lengths uniform in [256, 4096])."""
+    w = synth.WORKLOADS["doc_packed"]
+    lens = synth.doc_lengths(w.S, 256, 4096, w.seed)
+    ids = torch.from_numpy(synth.doc_ids_from_lengths(lens)).to(torch.int32)[None]
+    bm = fa.build_block_mask(3, 1, w.S, w.S, doc_ids=dev(ids))
+    torch.cuda.synchronize()
+    var = oracle.Variant(mask=3, doc_ids=ids.numpy())
+    # brute force on a band of query tiles (full check of every tile in them)
+    st = bm.tile_state.cpu().numpy()[0]
+    for qt in (0, 1, 37, 128, 200, 255):
+        rows = np.arange(qt * 128, qt * 128 + 128)
+        ok = oracle.allowed(var, 0, rows, np.arange(w.S))
+        for kt in range(256):
+            blk = ok[:, kt * 128:(kt + 1) * 128]
+            want = 0 if not blk.any() else (2 if blk.all() else 1)
+            assert st[qt, kt] == want, (qt, kt)
+
+
+@pytest.mark.parametrize("case", [2, 4, 7])
+def test_visited_with_block_mask(case):
+    """With a block mask the kernel processes exactly the listed blocks:
+    128/step key steps per listed block, minus steps past Skv."""
+    spec, B, Sq, Skv = CASES[case]
+    doc = _docs(B, Sq, 40 + case) if spec["mask"] == 3 else None
+    H = 2
+    q, k, v = (dev(t) for t in synth.qkv(B, H, H, Sq, Skv, 128, 1))
+    bm = fa.build_block_mask(spec["mask"], B, Sq, Skv, window=spec.get("window", 0), doc_ids=dev(doc))
+    nq = -(-Sq // 128)
+    vis = torch.zeros((B, H, nq), dtype=torch.int32, device="cuda")
+    fa.forward(q, k, v, doc_ids=dev(doc), block_mask=bm, visited=vis, **spec)
+    torch.cuda.synchronize()
+    step = fa.fa_fwd_kv_step(128, fa.FA_BF16)
+    var = oracle.Variant(doc_ids=None if doc is None else doc.numpy(), **spec)
+    _, kvl, _ = oracle.tile_states(var, B, Sq, Skv, 128, 128)
+    for b in range(B):
+        lists = kvl[b if spec["mask"] == 3 else 0]
+        for qt in range(nq):
+            want = sum(sum(1 for s0 in range(kt * 128, kt * 128 + 128, step) if s0 < Skv) for kt in lists[qt])
+            for h in range(H):
+                assert int(vis[b, h, qt]) == want

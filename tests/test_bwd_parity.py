@@ -1,0 +1,80 @@
+"""Backward pass: HIP library against the fp64 oracle's chain-rule gradients."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import tiled_attention_fa_amd as fa
+from tests.gpu_util import check_out, dev, f32_scale
+from tests.test_fwd_parity import VARIANTS, doc_ids_for
+
+pytestmark = pytest.mark.gpu
+
+
+def run_bwd(B, Hq, Hkv, S, D, spec, seed, block_mask=False):
+    q, k, v = synth.qkv(B, Hq, Hkv, S, S, D, seed)
+    do = synth.randn((B, Hq, S, D), seed + 100)
+    scale = f32_scale(D)
+    doc = doc_ids_for(B, S, seed) if spec.get("mask") == 3 else None
+    var = oracle.Variant(doc_ids=None if doc is None else doc.numpy(), **spec)
+    bm = None
+    if block_mask:
+        bm = fa.build_block_mask(spec.get("mask", 0), B, S, S, window=spec.get("window", 0), doc_ids=dev(doc))
+    qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
+    o, lse = fa.forward(qd, kd, vd, scale=scale, doc_ids=dev(doc), return_lse=True, block_mask=bm, **spec)
+    dq, dk, dv = fa.backward(qd, kd, vd, o, dod, lse, scale=scale, doc_ids=dev(doc), block_mask=bm, **spec)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.backward(q, k, v, do, scale, var)
+    return (dq, dk, dv), (rq, rk, rv)
+
+
+@pytest.mark.parametrize("name", sorted(VARIANTS))
+@pytest.mark.parametrize("D", [64, 128])
+def test_variants(name, D):
+    got, ref = run_bwd(1, 4, 2, 333, D, VARIANTS[name], seed=21)
+    for g, r, what in zip(got, ref, ("dQ", "dK", "dV")):
+        check_out(g, r, "bf16", what)
+
+
+@pytest.mark.parametrize("S", [1, 64, 127, 129, 260])
+def test_lengths_causal(S):
+    got, ref = run_bwd(1, 2, 2, S, 128, dict(mask=1), seed=S + 3)
+    for g, r, what in zip(got, ref, ("dQ", "dK", "dV")):
+        check_out(g, r, "bf16", what)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (4, 2), (4, 1)])
+def test_gqa_group_sums(Hq, Hkv):
+    got, ref = run_bwd(2, Hq, Hkv, 200, 128, dict(mask=1, mod=1), seed=7)
+    for g, r, what in zip(got, ref, ("dQ", "dK", "dV")):
+        check_out(g, r, "bf16", what)
+
+
+@pytest.mark.parametrize("name", ["causal", "document", "window_boost", "none"])
+def test_block_mask_path(name):
+    got, ref = run_bwd(1, 2, 2, 600, 128, VARIANTS[name], seed=8, block_mask=True)
+    for g, r, what in zip(got, ref, ("dQ", "dK", "dV")):
+        check_out(g, r, "bf16", what)
+
+
+def test_deterministic():
+    q, k, v = (dev(t) for t in synth.qkv(1, 4, 2, 400, 400, 128, 30))
+    do = dev(synth.randn((1, 4, 400, 128), 31))
+    o, lse = fa.forward(q, k, v, mask=1, return_lse=True)
+    a = fa.backward(q, k, v, o, do, lse, mask=1)
+    b = fa.backward(q, k, v, o, do, lse, mask=1)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_empty_queries_zero_key_grads():
+    """Sq = 0: no query sees any key, so dK = dV = 0."""
+    q = torch.empty((1, 2, 0, 64), dtype=torch.bfloat16, device="cuda")
+    k = torch.randn(1, 2, 50, 64, device="cuda").to(torch.bfloat16)
+    dk = torch.full_like(k, 7.0)
+    dv = torch.full_like(k, 7.0)
+    fa.backward(q, k, k, q, q, torch.empty((1, 2, 0), device="cuda"), grads=(q, dk, dv))
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)

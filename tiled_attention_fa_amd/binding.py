@@ -1,0 +1,231 @@
+"""ctypes binding of libmiattn (the C ABI in include/libmiattn.h).
+
+The functions ``fa_fwd``, ``fa_bwd``, ``fa_block_mask_build`` and the
+helpers mirror the C entry points one to one and take raw device pointers.
+``forward``, ``backward`` and ``build_block_mask`` are conveniences on top:
+they allocate outputs with torch, pass ``data_ptr()`` and the current stream,
+and raise ``FaError`` on a non-zero status.  No arithmetic of the method runs
+here; if the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmiattn.so")
+
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED = 0, -1, -2, -3
+FA_ERR_ALIGN, FA_ERR_PARAM, FA_ERR_WORKSPACE, FA_ERR_LAUNCH = -4, -5, -6, -7
+FA_BF16, FA_F32 = 0, 1
+MASK_NONE, MASK_CAUSAL, MASK_SLIDING_WINDOW, MASK_DOCUMENT = 0, 1, 2, 3
+MOD_NONE, MOD_ALIBI, MOD_SOFTCAP, MOD_LOCAL_BOOST = 0, 1, 2, 3
+TILE_EMPTY, TILE_PARTIAL, TILE_FULL = 0, 1, 2
+BLOCK = 128
+
+EXPORTED = ("fa_fwd", "fa_fwd_kv_step", "fa_bwd", "fa_bwd_workspace_bytes",
+            "fa_block_mask_build", "fa_status_str", "fa_version")
+
+
+class FaMaskParams(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("doc_ids", ctypes.c_void_p), ("visited", ctypes.c_void_p)]
+
+
+class FaModParams(ctypes.Structure):
+    _fields_ = [("alibi_slopes", ctypes.c_void_p), ("softcap", ctypes.c_float),
+                ("boost_radius", ctypes.c_int32), ("boost_factor", ctypes.c_float)]
+
+
+class FaBlockMask(ctypes.Structure):
+    _fields_ = [("block_q", ctypes.c_int32), ("block_kv", ctypes.c_int32),
+                ("n_q", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("n_b", ctypes.c_int32),
+                ("tile_state", ctypes.c_void_p), ("kv_count", ctypes.c_void_p),
+                ("kv_index", ctypes.c_void_p), ("q_count", ctypes.c_void_p),
+                ("q_index", ctypes.c_void_p)]
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {fa_status_str(status)} (status {status})")
+        self.status = status
+
+
+_LIB = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m tiled_attention_fa_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.fa_fwd.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
+                             _I, ctypes.POINTER(FaMaskParams), _I, ctypes.POINTER(FaModParams),
+                             ctypes.POINTER(FaBlockMask), _P]
+        L.fa_fwd.restype = _I
+        L.fa_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                             _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
+                             _I, ctypes.POINTER(FaMaskParams), _I, ctypes.POINTER(FaModParams),
+                             ctypes.POINTER(FaBlockMask), _P]
+        L.fa_bwd.restype = _I
+        L.fa_bwd_workspace_bytes.argtypes = [_I, _I, _I, _I]
+        L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.fa_block_mask_build.argtypes = [_I, ctypes.POINTER(FaMaskParams), _I, _I, _I,
+                                          ctypes.POINTER(FaBlockMask), _P]
+        L.fa_block_mask_build.restype = _I
+        L.fa_status_str.argtypes = [_I]
+        L.fa_status_str.restype = ctypes.c_char_p
+        L.fa_fwd_kv_step.argtypes = [_I, _I]
+        L.fa_fwd_kv_step.restype = _I
+        L.fa_version.argtypes = []
+        L.fa_version.restype = _I
+        _LIB = L
+    return _LIB
+
+
+# ---------------------------------------------------------------- raw C calls
+
+def fa_fwd(*args) -> int:
+    return lib().fa_fwd(*args)
+
+
+def fa_bwd(*args) -> int:
+    return lib().fa_bwd(*args)
+
+
+def fa_block_mask_build(*args) -> int:
+    return lib().fa_block_mask_build(*args)
+
+
+def fa_bwd_workspace_bytes(B: int, Hq: int, Sq: int, D: int) -> int:
+    return int(lib().fa_bwd_workspace_bytes(B, Hq, Sq, D))
+
+
+def fa_fwd_kv_step(D: int, dtype: int) -> int:
+    return int(lib().fa_fwd_kv_step(D, dtype))
+
+
+def fa_status_str(status: int) -> str:
+    return lib().fa_status_str(status).decode()
+
+
+def fa_version() -> int:
+    return int(lib().fa_version())
+
+
+# ---------------------------------------------------------------- torch conveniences
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def default_scale(D: int) -> float:
+    """1/sqrt(D) as the float32 value the kernel receives."""
+    return float(ctypes.c_float(1.0 / math.sqrt(D)).value)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _params(mask, window, doc_ids, visited, mod, alibi_slopes, softcap, boost_radius, boost_factor):
+    mp = FaMaskParams(int(window), None if doc_ids is None else doc_ids.data_ptr(),
+                      None if visited is None else visited.data_ptr())
+    op = FaModParams(None if alibi_slopes is None else alibi_slopes.data_ptr(), float(softcap),
+                     int(boost_radius), float(boost_factor))
+    return mp, op
+
+
+class BlockMask:
+    """Device arrays of a 128 x 128 block mask (owned by torch tensors)."""
+
+    def __init__(self, n_b, n_q, n_kv, device):
+        torch = _torch()
+        self.n_b, self.n_q, self.n_kv = n_b, n_q, n_kv
+        self.tile_state = torch.empty((n_b, n_q, n_kv), dtype=torch.uint8, device=device)
+        self.kv_count = torch.empty((n_b, n_q), dtype=torch.int32, device=device)
+        self.kv_index = torch.empty((n_b, n_q, max(n_kv, 1)), dtype=torch.int32, device=device)
+        self.q_count = torch.empty((n_b, n_kv), dtype=torch.int32, device=device)
+        self.q_index = torch.empty((n_b, max(n_kv, 1), max(n_q, 1)), dtype=torch.int32, device=device)
+
+    def struct(self) -> FaBlockMask:
+        return FaBlockMask(BLOCK, BLOCK, self.n_q, self.n_kv, self.n_b,
+                           self.tile_state.data_ptr(), self.kv_count.data_ptr(), self.kv_index.data_ptr(),
+                           self.q_count.data_ptr(), self.q_index.data_ptr())
+
+
+def build_block_mask(mask: int, B: int, Sq: int, Skv: int, *, window: int = 0, doc_ids=None,
+                     device="cuda", stream=None) -> BlockMask:
+    n_b = B if mask == MASK_DOCUMENT else 1
+    bm = BlockMask(n_b, -(-Sq // BLOCK), -(-Skv // BLOCK), device)
+    mp, _ = _params(mask, window, doc_ids, None, MOD_NONE, None, 0.0, 0, 1.0)
+    s = bm.struct()
+    rc = fa_block_mask_build(int(mask), ctypes.byref(mp), int(B), int(Sq), int(Skv), ctypes.byref(s), _stream(stream))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_block_mask_build")
+    return bm
+
+
+def forward(q, k, v, *, scale=None, mask=MASK_NONE, window=0, doc_ids=None, mod=MOD_NONE,
+            alibi_slopes=None, softcap=0.0, boost_radius=0, boost_factor=1.0, block_mask=None,
+            return_lse=False, out=None, lse=None, visited=None, stream=None):
+    """O (and LSE if ``return_lse``) for q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] on the GPU."""
+    torch = _torch()
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    mp, op = _params(mask, window, doc_ids, visited, mod, alibi_slopes, softcap, boost_radius, boost_factor)
+    bms = block_mask.struct() if block_mask is not None else None
+    rc = fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse) if return_lse else None,
+                B, Hq, Hkv, Sq, Skv, D, _dtype_code(q), float(default_scale(D) if scale is None else scale),
+                int(mask), ctypes.byref(mp), int(mod), ctypes.byref(op),
+                ctypes.byref(bms) if bms is not None else None, _stream(stream))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_fwd")
+    return (out, lse) if return_lse else out
+
+
+def backward(q, k, v, out, dout, lse, *, scale=None, mask=MASK_NONE, window=0, doc_ids=None,
+             mod=MOD_NONE, alibi_slopes=None, softcap=0.0, boost_radius=0, boost_factor=1.0,
+             block_mask=None, workspace=None, grads=None, stream=None):
+    """(dq, dk, dv) of sum(O * dout), recomputing P from ``lse``."""
+    torch = _torch()
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    ws_bytes = fa_bwd_workspace_bytes(B, Hq, Sq, D)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    mp, op = _params(mask, window, doc_ids, None, mod, alibi_slopes, softcap, boost_radius, boost_factor)
+    bms = block_mask.struct() if block_mask is not None else None
+    rc = fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                B, Hq, Hkv, Sq, Skv, D, _dtype_code(q), float(default_scale(D) if scale is None else scale),
+                int(mask), ctypes.byref(mp), int(mod), ctypes.byref(op),
+                ctypes.byref(bms) if bms is not None else None, _stream(stream))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_bwd")
+    return dq, dk, dv

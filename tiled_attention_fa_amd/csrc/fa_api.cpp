@@ -1,0 +1,252 @@
+// C ABI of libmiattn: argument validation (before any HIP call) and
+// dispatch to the template instantiations.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/libmiattn.h"
+#include "fa_args.h"
+#include "fa_launch.h"
+
+using namespace miattn;
+
+namespace {
+
+constexpr long long kMaxSeq = 1LL << 22;    // 4M tokens per sequence
+constexpr long long kMaxGrid = 0x7fffffffLL;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
+
+int check_shapes(int B, int Hq, int Hkv, int Sq, int Skv, int D) {
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  if (B < 0 || Sq < 0 || Skv < 0 || Hq < 1 || Hkv < 1) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (Sq > kMaxSeq || Skv > kMaxSeq || Hq > 65536) return FA_ERR_SHAPE;
+  const long long heads = (long long)B * Hq;
+  if (heads * cdiv(Sq, kTileQ) > kMaxGrid || (long long)B * Hkv * cdiv(Skv, kTileQ) > kMaxGrid) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+// Checks shared by the forward and backward passes; fills the mask and
+// modifier argument blocks.
+int check_variant(int B, int Hq, int Sq, int Skv, float scale, int mask_kind, const fa_mask_params* mp,
+                  int mod_kind, const fa_mod_params* op, MaskArgs& mask, ModArgs& mod) {
+  if (!std::isfinite(scale) || scale < 0.0f) return FA_ERR_PARAM;
+  mask = MaskArgs{0, nullptr};
+  mod = ModArgs{nullptr, 1.0f, 1.0f, 0, 1.0f};
+  switch (mask_kind) {
+    case FA_MASK_NONE:
+    case FA_MASK_CAUSAL: break;
+    case FA_MASK_SLIDING_WINDOW:
+      if (!mp) return FA_ERR_NULL;
+      if (mp->window < 1) return FA_ERR_PARAM;
+      mask.window = mp->window;
+      break;
+    case FA_MASK_DOCUMENT:
+      if (!mp || !mp->doc_ids) return FA_ERR_NULL;
+      if (!aligned(mp->doc_ids, 4)) return FA_ERR_ALIGN;
+      if (Sq != Skv) return FA_ERR_SHAPE;
+      mask.doc_ids = mp->doc_ids;
+      break;
+    default: return FA_ERR_UNSUPPORTED;
+  }
+  switch (mod_kind) {
+    case FA_MOD_NONE: break;
+    case FA_MOD_ALIBI:
+      if (op && op->alibi_slopes) {
+        if (!aligned(op->alibi_slopes, 4)) return FA_ERR_ALIGN;
+        mod.slopes = op->alibi_slopes;
+      }
+      break;
+    case FA_MOD_SOFTCAP:
+      if (!op) return FA_ERR_NULL;
+      if (!std::isfinite(op->softcap) || !(op->softcap > 0.0f)) return FA_ERR_PARAM;
+      mod.softcap = op->softcap;
+      mod.inv_softcap = 1.0f / op->softcap;
+      break;
+    case FA_MOD_LOCAL_BOOST:
+      if (!op) return FA_ERR_NULL;
+      if (op->boost_radius < 0 || !std::isfinite(op->boost_factor)) return FA_ERR_PARAM;
+      mod.boost_radius = op->boost_radius;
+      mod.boost_factor = op->boost_factor;
+      break;
+    default: return FA_ERR_UNSUPPORTED;
+  }
+  (void)B;
+  (void)Hq;
+  return FA_OK;
+}
+
+int check_block_mask(const fa_block_mask* bm, int mask_kind, int B, int Sq, int Skv, bool need_q_lists,
+                     BlockMaskArgs& out) {
+  out = BlockMaskArgs{nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 0};
+  if (!bm) return FA_OK;
+  if (bm->block_q != kMaskBlock || bm->block_kv != kMaskBlock) return FA_ERR_UNSUPPORTED;
+  if (bm->n_q != cdiv(Sq, kMaskBlock) || bm->n_kv != cdiv(Skv, kMaskBlock)) return FA_ERR_SHAPE;
+  if (!(bm->n_b == 1 || bm->n_b == B)) return FA_ERR_SHAPE;
+  if (mask_kind == FA_MASK_DOCUMENT && bm->n_b != B) return FA_ERR_SHAPE;
+  if (!bm->tile_state || !bm->kv_count || !bm->kv_index) return FA_ERR_NULL;
+  if (need_q_lists && (!bm->q_count || !bm->q_index)) return FA_ERR_NULL;
+  if (!aligned(bm->kv_count, 4) || !aligned(bm->kv_index, 4)) return FA_ERR_ALIGN;
+  if (need_q_lists && (!aligned(bm->q_count, 4) || !aligned(bm->q_index, 4))) return FA_ERR_ALIGN;
+  out = BlockMaskArgs{bm->tile_state, bm->kv_count, bm->kv_index, bm->q_count, bm->q_index,
+                      bm->n_b, bm->n_q, bm->n_kv};
+  return FA_OK;
+}
+
+int check_tensor(const void* p, bool nonempty) {
+  if (!nonempty) return FA_OK;
+  if (!p) return FA_ERR_NULL;
+  if (!aligned(p, 16)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return 100; }
+
+const char* fa_status_str(int s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "sizes are negative, inconsistent or too large";
+    case FA_ERR_UNSUPPORTED: return "head dim, dtype or combination not supported";
+    case FA_ERR_ALIGN: return "a device pointer is misaligned";
+    case FA_ERR_PARAM: return "a mask or modifier parameter is out of range";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int fa_fwd_kv_step(int D, int dtype) {
+  if ((D != 64 && D != 128) || (dtype != FA_BF16 && dtype != FA_F32)) return FA_ERR_UNSUPPORTED;
+  return fwd_kv_step(dtype == FA_F32);
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int Sq,
+           int Skv, int D, int dtype, float scale, int mask_kind, const fa_mask_params* mask_params,
+           int score_mod_kind, const fa_mod_params* mod_params, const fa_block_mask* block_mask, void* stream) {
+  if (dtype != FA_BF16 && dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  int rc = check_shapes(B, Hq, Hkv, Sq, Skv, D);
+  if (rc) return rc;
+  FwdArgs a{};
+  rc = check_variant(B, Hq, Sq, Skv, scale, mask_kind, mask_params, score_mod_kind, mod_params, a.mask, a.mod);
+  if (rc) return rc;
+  rc = check_block_mask(block_mask, mask_kind, B, Sq, Skv, false, a.bm);
+  if (rc) return rc;
+  const bool has_q = (long long)B * Sq > 0, has_kv = (long long)B * Skv > 0;
+  if ((rc = check_tensor(q, has_q)) || (rc = check_tensor(out, has_q)) || (rc = check_tensor(k, has_kv)) ||
+      (rc = check_tensor(v, has_kv)))
+    return rc;
+  if (lse && !aligned(lse, 4)) return FA_ERR_ALIGN;
+  int32_t* visited = mask_params ? mask_params->visited : nullptr;
+  if (visited && !aligned(visited, 4)) return FA_ERR_ALIGN;
+  if (!has_q) return FA_OK;
+
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.lse = lse;
+  a.visited = visited;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.Sq = Sq;
+  a.Skv = Skv;
+  a.n_qt = (int)cdiv(Sq, kTileQ);
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == FA_BF16)
+    e = D == 128 ? launch_fwd_dt<128, false>(a, mask_kind, score_mod_kind, st)
+                 : launch_fwd_dt<64, false>(a, mask_kind, score_mod_kind, st);
+  else
+    e = D == 128 ? launch_fwd_dt<128, true>(a, mask_kind, score_mod_kind, st)
+                 : launch_fwd_dt<64, true>(a, mask_kind, score_mod_kind, st);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq, int D) {
+  (void)D;
+  if (B <= 0 || Hq <= 0 || Sq <= 0) return 256;
+  const size_t n = (size_t)B * Hq * Sq * sizeof(float);
+  return (n + 255) & ~(size_t)255;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+           void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes, int B, int Hq, int Hkv, int Sq, int Skv,
+           int D, int dtype, float scale, int mask_kind, const fa_mask_params* mask_params, int score_mod_kind,
+           const fa_mod_params* mod_params, const fa_block_mask* block_mask, void* stream) {
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  int rc = check_shapes(B, Hq, Hkv, Sq, Skv, D);
+  if (rc) return rc;
+  BwdArgs a{};
+  rc = check_variant(B, Hq, Sq, Skv, scale, mask_kind, mask_params, score_mod_kind, mod_params, a.mask, a.mod);
+  if (rc) return rc;
+  rc = check_block_mask(block_mask, mask_kind, B, Sq, Skv, true, a.bm);
+  if (rc) return rc;
+  const bool has_q = (long long)B * Sq > 0, has_kv = (long long)B * Skv > 0;
+  if ((rc = check_tensor(q, has_q)) || (rc = check_tensor(out, has_q)) || (rc = check_tensor(dout, has_q)) ||
+      (rc = check_tensor(dq, has_q)) || (rc = check_tensor(k, has_kv)) || (rc = check_tensor(v, has_kv)) ||
+      (rc = check_tensor(dk, has_kv)) || (rc = check_tensor(dv, has_kv)))
+    return rc;
+  if (has_q) {
+    if (!lse) return FA_ERR_NULL;
+    if (!aligned(lse, 4)) return FA_ERR_ALIGN;
+    if (!workspace || ws_bytes < fa_bwd_workspace_bytes(B, Hq, Sq, D)) return FA_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
+  }
+  if (B == 0) return FA_OK;
+
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = (float*)workspace;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.Sq = Sq;
+  a.Skv = Skv;
+  a.n_qt = (int)cdiv(Sq, kTileQ);
+  a.n_kt = (int)cdiv(Skv, kTileQ);
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = D == 128 ? launch_bwd_d<128>(a, mask_kind, score_mod_kind, st)
+                                : launch_bwd_d<64>(a, mask_kind, score_mod_kind, st);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_block_mask_build(int mask_kind, const fa_mask_params* mask_params, int B, int Sq, int Skv,
+                        const fa_block_mask* out, void* stream) {
+  if (!out) return FA_ERR_NULL;
+  if (B < 1 || Sq < 0 || Skv < 0 || Sq > kMaxSeq || Skv > kMaxSeq) return FA_ERR_SHAPE;
+  MaskArgs mask;
+  ModArgs mod;
+  int rc = check_variant(B, 1, Sq, Skv, 1.0f, mask_kind, mask_params, FA_MOD_NONE, nullptr, mask, mod);
+  if (rc) return rc;
+  BlockMaskArgs m;
+  rc = check_block_mask(out, mask_kind, B, Sq, Skv, true, m);
+  if (rc) return rc;
+  if (m.n_b > 65535) return FA_ERR_SHAPE;
+  const hipError_t e = launch_block_mask(mask_kind, mask.window, mask.doc_ids, Sq, Skv, m,
+                                         reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Kernel argument blocks shared by the host dispatcher and the kernels.
+#pragma once
+#include <stdint.h>
+
+namespace miattn {
+
+enum { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_WINDOW = 2, MASK_DOCUMENT = 3 };
+enum { MOD_NONE = 0, MOD_ALIBI = 1, MOD_SOFTCAP = 2, MOD_BOOST = 3 };
+enum { TILE_EMPTY = 0, TILE_PARTIAL = 1, TILE_FULL = 2 };
+
+// Query rows per workgroup and the block-mask granularity; the forward,
+// backward and block-mask kernels all use 128-row query tiles.
+constexpr int kTileQ = 128;
+constexpr int kMaskBlock = 128;
+
+struct MaskArgs {
+  int window;
+  const int32_t* doc_ids;  // [B][S]
+};
+
+struct ModArgs {
+  const float* slopes;  // [Hq] or null: 2^(-8(h+1)/Hq)
+  float softcap, inv_softcap;
+  int boost_radius;
+  float boost_factor;
+};
+
+struct BlockMaskArgs {
+  uint8_t* tile_state;  // null: tile ranges follow from the mask kind
+  int32_t* kv_count;    // the attention kernels only read these arrays;
+  int32_t* kv_index;    // the block-mask builder writes them
+  int32_t* q_count;
+  int32_t* q_index;
+  int n_b, n_q, n_kv;
+};
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int32_t* visited;
+  int B, Hq, Hkv, G, Sq, Skv;
+  int n_qt;  // query tiles of kTileQ rows
+  float scale, scale_log2;
+  MaskArgs mask;
+  ModArgs mod;
+  BlockMaskArgs bm;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* delta;  // [B][Hq][Sq] workspace: rowsum(dO * O)
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, Hq, Hkv, G, Sq, Skv;
+  int n_qt, n_kt;
+  float scale, scale_log2;
+  MaskArgs mask;
+  ModArgs mod;
+  BlockMaskArgs bm;
+};
+
+}  // namespace miattn

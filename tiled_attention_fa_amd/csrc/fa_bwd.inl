@@ -1,0 +1,539 @@
+// Backward attention kernels for gfx950 (included by fa_bwd_d*.hip).
+//
+// The backward pass recomputes the probabilities from Q, K and the saved
+// LSE instead of storing the score matrix ("FlashAttention-2" page, §3
+// recomputation and §4 backward).  The gradient formulas are not on the
+// pages; they are the chain rule of the forward definition:
+//   P = exp(mod(scale q.k) - LSE), dV = P^T dO, dP = dO V^T,
+//   delta_i = rowsum(dO_i * O_i), dS = P (dP - delta) mod',
+//   dQ = scale dS K, dK = scale dS^T Q.
+// Three launches on one stream: delta, then a key-stationary kernel that
+// owns 128 keys and loops over every query head of its GQA group and every
+// query step (dK, dV accumulated in registers, written once), then a
+// query-stationary kernel for dQ (like the forward pass).  Nothing is
+// accumulated with atomics, so the results are deterministic.
+#include "fa_device.h"
+
+namespace miattn {
+
+// ---------------------------------------------------------------- delta
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restrict__ o,
+                                                        const uint16_t* __restrict__ dout,
+                                                        float* __restrict__ delta, long rows) {
+  constexpr int LPR = D / 8;  // lanes per row, 16 bytes each
+  const long row = (long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int c = threadIdx.x % LPR;
+  float s = 0.0f;
+  if (row < rows) {
+    const u32x4 x = *(const u32x4*)(o + row * D + c * 8);
+    const u32x4 y = *(const u32x4*)(dout + row * D + c * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s += bf16_lo(x[e]) * bf16_lo(y[e]) + bf16_hi(x[e]) * bf16_hi(y[e]);
+  }
+#pragma unroll
+  for (int w = LPR / 2; w >= 1; w >>= 1) s += __shfl_xor(s, w, LPR);
+  if (row < rows && c == 0) delta[row] = s;
+}
+
+// Probability, and the factor that turns dP - delta into dS, for one
+// (query i, key j) score: x2 is the modified score in log2 units.
+template <int MOD>
+__device__ __forceinline__ void recompute_p(float sraw, int i, int j, float slope, const BwdArgs& a,
+                                            float lse2, float& p, float& grad) {
+  float x2;
+  grad = 1.0f;
+  if constexpr (MOD == MOD_NONE) {
+    x2 = sraw * a.scale_log2;
+  } else if constexpr (MOD == MOD_ALIBI) {
+    x2 = (sraw * a.scale + slope * (float)(j - i)) * kLog2e;
+  } else if constexpr (MOD == MOD_SOFTCAP) {
+    const float th = tanh_exp2(sraw * a.scale * a.mod.inv_softcap);
+    x2 = a.mod.softcap * th * kLog2e;
+    grad = 1.0f - th * th;
+  } else {
+    int d = i - j;
+    d = d < 0 ? -d : d;
+    grad = d < a.mod.boost_radius ? a.mod.boost_factor : 1.0f;
+    x2 = sraw * a.scale * grad * kLog2e;
+  }
+  p = fast_exp2(x2 - lse2);
+}
+
+// ---------------------------------------------------------------- dK, dV
+// Workgroup: 4 waves own keys [k0, k0 + 128), 32 per wave (one key column
+// per lane).  Per step: 64 query rows of one query head, Q and dO tiles in
+// LDS.  S = Q K^T and dP = dO V^T come out key-column-per-lane, so P and
+// dS are repacked in registers as the B operands of dV^T += dO^T P and
+// dK^T += Q^T dS, whose A operands are transposing LDS reads.
+template <int D, int MASK, int MOD>
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int BK = 128, BQ = 64, NQ = BQ / 32;
+  constexpr int ROW = D * 2, TILE = BQ * ROW;
+  constexpr int KC = D / 16, DT = D / 32, NCH = D / 8, LOADS = BQ * NCH / 256;
+  static_assert(LOADS * 256 == BQ * NCH, "tile load must divide evenly");
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];  // [stage][Q, dO]
+  __shared__ __attribute__((aligned(16))) float slse[2][BQ];
+  __shared__ __attribute__((aligned(16))) float sdel[2][BQ];
+  __shared__ int sdoc[2][BQ];
+
+  int b, hk, kt;
+  decode_work(blockIdx.x, a.B, a.Hkv, a.Hkv, a.n_kt, false, b, hk, kt);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int gi = lane & 15, g16 = (lane >> 4) & 1;
+  const int Sq = a.Sq, Skv = a.Skv, G = a.G, window = a.mask.window;
+  const int k0 = kt * BK, kw0 = k0 + 32 * wave, kj = kw0 + l32;
+  const bool col_ok = kj < Skv;
+
+  const uint16_t* Kh = (const uint16_t*)a.k + (size_t)(b * a.Hkv + hk) * Skv * D;
+  const uint16_t* Vh = (const uint16_t*)a.v + (size_t)(b * a.Hkv + hk) * Skv * D;
+  u32x4 kf[KC], vf[KC];
+  {
+    const u32x4* ks = (const u32x4*)(Kh + (size_t)(col_ok ? kj : 0) * D);
+    const u32x4* vs = (const u32x4*)(Vh + (size_t)(col_ok ? kj : 0) * D);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      kf[c] = col_ok ? ks[2 * c + hh] : u32x4{0, 0, 0, 0};
+      vf[c] = col_ok ? vs[2 * c + hh] : u32x4{0, 0, 0, 0};
+    }
+  }
+  const int32_t* doc = (MASK == MASK_DOCUMENT) ? a.mask.doc_ids + (size_t)b * Skv : nullptr;
+  int doc_j = 0;
+  if constexpr (MASK == MASK_DOCUMENT) doc_j = col_ok ? doc[kj] : -3;
+
+  // query steps per head
+  constexpr int STEPS_PER_BLOCK = kMaskBlock / BQ;
+  const bool use_bm = a.bm.tile_state != nullptr;
+  int qs_lo = 0, n_qs = 0;
+  const int32_t* bm_list = nullptr;
+  const uint8_t* bm_state = nullptr;
+  int bm_row = 0;
+  if (use_bm) {
+    const int bb = a.bm.n_b == 1 ? 0 : b;
+    n_qs = a.bm.q_count[bb * a.bm.n_kv + kt] * STEPS_PER_BLOCK;
+    bm_list = a.bm.q_index + (size_t)(bb * a.bm.n_kv + kt) * a.bm.n_q;
+    bm_state = a.bm.tile_state + (size_t)bb * a.bm.n_q * a.bm.n_kv;
+    bm_row = a.bm.n_kv;
+  } else {
+    int lo = 0, hi = Sq;
+    if constexpr (MASK != MASK_NONE) lo = min(k0, Sq);
+    if constexpr (MASK == MASK_WINDOW) hi = min(Sq, k0 + BK - 1 + window);
+    if (hi > lo) {
+      qs_lo = lo / BQ;
+      n_qs = (hi + BQ - 1) / BQ - qs_lo;
+    }
+  }
+  auto step_q0 = [&](int s) -> int {
+    const int qs = s % n_qs;
+    if (use_bm) return bm_list[qs / STEPS_PER_BLOCK] * kMaskBlock + (qs % STEPS_PER_BLOCK) * BQ;
+    return (qs_lo + qs) * BQ;
+  };
+  const int n_steps = G * n_qs;
+
+  u32x4 qr[LOADS], dr[LOADS];
+  float lr = 0.0f, er = 0.0f;
+  int docr = 0;
+  auto gload = [&](int s) {
+    const int hq = hk * G + s / n_qs, q0 = step_q0(s);
+    const uint16_t* Qh = (const uint16_t*)a.q + (size_t)(b * a.Hq + hq) * Sq * D;
+    const uint16_t* dOh = (const uint16_t*)a.dout + (size_t)(b * a.Hq + hq) * Sq * D;
+#pragma unroll
+    for (int p = 0; p < LOADS; ++p) {
+      const int id = tid + 256 * p, r = id / NCH, c = id % NCH, i = q0 + r;
+      if (i < Sq) {
+        qr[p] = *(const u32x4*)(Qh + (size_t)i * D + c * 8);
+        dr[p] = *(const u32x4*)(dOh + (size_t)i * D + c * 8);
+      } else {
+        qr[p] = u32x4{0, 0, 0, 0};
+        dr[p] = u32x4{0, 0, 0, 0};
+      }
+    }
+    if (tid < BQ) {
+      const int i = q0 + tid;
+      const size_t ri = (size_t)(b * a.Hq + hq) * Sq + i;
+      const float L = i < Sq ? a.lse[ri] : kNegInf;
+      // Rows past the end or with no admissible key contribute nothing.
+      lr = (L == kNegInf) ? __builtin_inff() : L * kLog2e;
+      er = i < Sq ? a.delta[ri] : 0.0f;
+      if constexpr (MASK == MASK_DOCUMENT) docr = i < Sq ? doc[i] : -4;
+    }
+  };
+  auto lstore = [&](int stage) {
+    char* qs = smem + stage * 2 * TILE;
+    char* ds = qs + TILE;
+#pragma unroll
+    for (int p = 0; p < LOADS; ++p) {
+      const int id = tid + 256 * p, r = id / NCH, c = id % NCH;
+      *(u32x4*)(qs + r * ROW + swz<D>(r, c) * 16) = qr[p];
+      *(u32x4*)(ds + r * ROW + swz<D>(r, c) * 16) = dr[p];
+    }
+    if (tid < BQ) {
+      slse[stage][tid] = lr;
+      sdel[stage][tid] = er;
+      if constexpr (MASK == MASK_DOCUMENT) sdoc[stage][tid] = docr;
+    }
+  };
+
+  f32x16 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dk[dt] = f32x16{};
+    dv[dt] = f32x16{};
+  }
+  if (n_steps > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int s = 0; s < n_steps; ++s) {
+    const int cur = s & 1;
+    const bool have_next = s + 1 < n_steps;
+    if (have_next) gload(s + 1);
+    const int hq = hk * G + s / n_qs;
+    const int q0 = step_q0(s);
+    int cls;
+    if (use_bm) {
+      const int qb = bm_list[(s % n_qs) / STEPS_PER_BLOCK];
+      cls = bm_state[qb * bm_row + kt] == TILE_FULL ? TILE_FULL : TILE_PARTIAL;
+    } else {
+      cls = block_class<MASK>(q0, BQ, kw0, 32, Skv, window);
+    }
+    if (kw0 >= Skv || q0 >= Sq) cls = TILE_EMPTY;
+
+    if (cls != TILE_EMPTY) {
+      const char* qs = smem + cur * 2 * TILE;
+      const char* ds = qs + TILE;
+      const float slope = head_slope<MOD>(a.mod, hq, a.Hq);
+      f32x16 sp[NQ], dp[NQ];
+#pragma unroll
+      for (int t = 0; t < NQ; ++t) {
+        sp[t] = f32x16{};
+        dp[t] = f32x16{};
+        const int r = 32 * t + l32;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          sp[t] = mfma_bf16(*(const u32x4*)(qs + r * ROW + swz<D>(r, 2 * c + hh) * 16), kf[c], sp[t]);
+          dp[t] = mfma_bf16(*(const u32x4*)(ds + r * ROW + swz<D>(r, 2 * c + hh) * 16), vf[c], dp[t]);
+        }
+      }
+      // P and dS (register r of subtile t: query q0 + 32t + 8(r/4) + 4hh + r%4)
+#pragma unroll
+      for (int t = 0; t < NQ; ++t)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int ir = 32 * t + 8 * rq + 4 * hh;
+          const f32x4 L4 = *(const f32x4*)&slse[cur][ir];
+          const f32x4 E4 = *(const f32x4*)&sdel[cur][ir];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = q0 + ir + e;
+            float p, grad;
+            recompute_p<MOD>(sp[t][4 * rq + e], i, kj, slope, a, L4[e], p, grad);
+            if (cls == TILE_PARTIAL) {
+              int di = 0;
+              if constexpr (MASK == MASK_DOCUMENT) di = sdoc[cur][ir + e];
+              const bool ok = col_ok && mask_ok<MASK>(i, kj, window, di, doc_j);
+              p = ok ? p : 0.0f;
+            }
+            sp[t][4 * rq + e] = p;
+            dp[t][4 * rq + e] = p * (dp[t][4 * rq + e] - E4[e]) * grad;
+          }
+        }
+      u32x4 pb[NQ][2], sb[NQ][2];
+#pragma unroll
+      for (int t = 0; t < NQ; ++t)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          pb[t][cc] = u32x4{pack_bf16(sp[t][8 * cc + 0], sp[t][8 * cc + 1]),
+                            pack_bf16(sp[t][8 * cc + 2], sp[t][8 * cc + 3]),
+                            pack_bf16(sp[t][8 * cc + 4], sp[t][8 * cc + 5]),
+                            pack_bf16(sp[t][8 * cc + 6], sp[t][8 * cc + 7])};
+          sb[t][cc] = u32x4{pack_bf16(dp[t][8 * cc + 0], dp[t][8 * cc + 1]),
+                            pack_bf16(dp[t][8 * cc + 2], dp[t][8 * cc + 3]),
+                            pack_bf16(dp[t][8 * cc + 4], dp[t][8 * cc + 5]),
+                            pack_bf16(dp[t][8 * cc + 6], dp[t][8 * cc + 7])};
+        }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int ch = 4 * dt + 2 * g16 + ((gi & 3) >> 1);
+        const int half = (gi & 1) * 8;
+#pragma unroll
+        for (int t = 0; t < NQ; ++t)
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const int r0 = 32 * t + 16 * cc + 4 * hh + (gi >> 2), r1 = r0 + 8;
+            const int o0 = r0 * ROW + swz<D>(r0, ch) * 16 + half, o1 = r1 * ROW + swz<D>(r1, ch) * 16 + half;
+            const u32x2 dlo = lds_read_tr16(ds + o0), dhi = lds_read_tr16(ds + o1);
+            dv[dt] = mfma_bf16(u32x4{dlo[0], dlo[1], dhi[0], dhi[1]}, pb[t][cc], dv[dt]);
+            const u32x2 qlo = lds_read_tr16(qs + o0), qhi = lds_read_tr16(qs + o1);
+            dk[dt] = mfma_bf16(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, sb[t][cc], dk[dt]);
+          }
+      }
+    }
+    if (have_next) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  if (col_ok) {
+    uint16_t* dK = (uint16_t*)a.dk + ((size_t)(b * a.Hkv + hk) * Skv + kj) * D;
+    uint16_t* dV = (uint16_t*)a.dv + ((size_t)(b * a.Hkv + hk) * Skv + kj) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d0 = 32 * dt + 8 * rq + 4 * hh;
+        *(u32x2*)(dK + d0) = u32x2{pack_bf16(dk[dt][4 * rq] * a.scale, dk[dt][4 * rq + 1] * a.scale),
+                                   pack_bf16(dk[dt][4 * rq + 2] * a.scale, dk[dt][4 * rq + 3] * a.scale)};
+        *(u32x2*)(dV + d0) = u32x2{pack_bf16(dv[dt][4 * rq], dv[dt][4 * rq + 1]),
+                                   pack_bf16(dv[dt][4 * rq + 2], dv[dt][4 * rq + 3])};
+      }
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+// Workgroup: 4 waves own 128 query rows of one head, 32 per wave (one query
+// column per lane, as in the forward kernel).  Per step: 64 keys, K and V
+// tiles in LDS.  S^T = K Q^T and dP^T = V dO^T give dS^T with a query per
+// lane; dQ^T += K^T dS^T takes K^T from transposing LDS reads.
+template <int D, int MASK, int MOD>
+__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int BN = 64, NT = BN / 32;
+  constexpr int ROW = D * 2, TILE = BN * ROW;
+  constexpr int KC = D / 16, DT = D / 32, NCH = D / 8, LOADS = BN * NCH / 256;
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];  // [stage][K, V]
+  __shared__ int sdoc[2][BN];
+
+  int b, hq, qt;
+  decode_work(blockIdx.x, a.B, a.Hq, a.Hkv, a.n_qt, MASK == MASK_CAUSAL || MASK == MASK_DOCUMENT, b, hq,
+              qt);
+  const int hk = hq / a.G;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int gi = lane & 15, g16 = (lane >> 4) & 1;
+  const int Sq = a.Sq, Skv = a.Skv, window = a.mask.window;
+  const int q0 = qt * kTileQ, qw0 = q0 + 32 * wave, qi = qw0 + l32;
+  const bool row_ok = qi < Sq;
+
+  const size_t ri = (size_t)(b * a.Hq + hq) * Sq + (row_ok ? qi : 0);
+  const uint16_t* Qrow = (const uint16_t*)a.q + ri * D;
+  const uint16_t* dOrow = (const uint16_t*)a.dout + ri * D;
+  u32x4 qf[KC], of[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    qf[c] = row_ok ? ((const u32x4*)Qrow)[2 * c + hh] : u32x4{0, 0, 0, 0};
+    of[c] = row_ok ? ((const u32x4*)dOrow)[2 * c + hh] : u32x4{0, 0, 0, 0};
+  }
+  float lse2 = __builtin_inff(), del = 0.0f;
+  if (row_ok) {
+    const float L = a.lse[ri];
+    lse2 = (L == kNegInf) ? __builtin_inff() : L * kLog2e;
+    del = a.delta[ri];
+  }
+  const uint16_t* K = (const uint16_t*)a.k + (size_t)(b * a.Hkv + hk) * Skv * D;
+  const uint16_t* V = (const uint16_t*)a.v + (size_t)(b * a.Hkv + hk) * Skv * D;
+  const int32_t* doc = nullptr;
+  int doc_i = 0;
+  if constexpr (MASK == MASK_DOCUMENT) {
+    doc = a.mask.doc_ids + (size_t)b * Skv;
+    doc_i = row_ok ? doc[qi] : -1;
+  }
+  const float slope = head_slope<MOD>(a.mod, hq, a.Hq);
+
+  constexpr int STEPS_PER_BLOCK = kMaskBlock / BN;
+  const bool use_bm = a.bm.tile_state != nullptr;
+  int step_lo = 0, n_steps = 0;
+  const int32_t* bm_list = nullptr;
+  const uint8_t* bm_state = nullptr;
+  if (use_bm) {
+    const int bb = a.bm.n_b == 1 ? 0 : b;
+    const int row = bb * a.bm.n_q + qt;
+    n_steps = a.bm.kv_count[row] * STEPS_PER_BLOCK;
+    bm_list = a.bm.kv_index + (size_t)row * a.bm.n_kv;
+    bm_state = a.bm.tile_state + (size_t)row * a.bm.n_kv;
+  } else {
+    int lo, hi;
+    key_range<MASK>(q0, min(q0 + kTileQ, Sq), Skv, window, lo, hi);
+    if (hi > lo) {
+      step_lo = lo / BN;
+      n_steps = (hi + BN - 1) / BN - step_lo;
+    }
+  }
+  auto step_k0 = [&](int s) -> int {
+    if (use_bm) return bm_list[s / STEPS_PER_BLOCK] * kMaskBlock + (s % STEPS_PER_BLOCK) * BN;
+    return (step_lo + s) * BN;
+  };
+
+  u32x4 kr[LOADS], vr[LOADS];
+  int docr = 0;
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int p = 0; p < LOADS; ++p) {
+      const int id = tid + 256 * p, r = id / NCH, c = id % NCH, j = k0 + r;
+      if (j < Skv) {
+        kr[p] = *(const u32x4*)(K + (size_t)j * D + c * 8);
+        vr[p] = *(const u32x4*)(V + (size_t)j * D + c * 8);
+      } else {
+        kr[p] = u32x4{0, 0, 0, 0};
+        vr[p] = u32x4{0, 0, 0, 0};
+      }
+    }
+    if constexpr (MASK == MASK_DOCUMENT) {
+      if (tid < BN) docr = (k0 + tid < Skv) ? doc[k0 + tid] : -2;
+    }
+  };
+  auto lstore = [&](int stage) {
+    char* ks = smem + stage * 2 * TILE;
+    char* vs = ks + TILE;
+#pragma unroll
+    for (int p = 0; p < LOADS; ++p) {
+      const int id = tid + 256 * p, r = id / NCH, c = id % NCH;
+      *(u32x4*)(ks + r * ROW + swz<D>(r, c) * 16) = kr[p];
+      *(u32x4*)(vs + r * ROW + swz<D>(r, c) * 16) = vr[p];
+    }
+    if constexpr (MASK == MASK_DOCUMENT) {
+      if (tid < BN) sdoc[stage][tid] = docr;
+    }
+  };
+
+  f32x16 dq[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x16{};
+  if (n_steps > 0) {
+    gload(step_k0(0));
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int s = 0; s < n_steps; ++s) {
+    const int cur = s & 1;
+    const int k0 = step_k0(s);
+    const bool have_next = s + 1 < n_steps;
+    if (have_next) gload(step_k0(s + 1));
+    int cls;
+    if (use_bm) {
+      cls = (k0 >= Skv) ? TILE_EMPTY
+                        : (bm_state[bm_list[s / STEPS_PER_BLOCK]] == TILE_FULL ? TILE_FULL : TILE_PARTIAL);
+    } else {
+      cls = block_class<MASK>(qw0, 32, k0, BN, Skv, window);
+    }
+    if (qw0 >= Sq) cls = TILE_EMPTY;
+
+    if (cls != TILE_EMPTY) {
+      const char* ks = smem + cur * 2 * TILE;
+      const char* vs = ks + TILE;
+      f32x16 st[NT], dpt[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        st[t] = f32x16{};
+        dpt[t] = f32x16{};
+        const int r = 32 * t + l32;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          st[t] = mfma_bf16(*(const u32x4*)(ks + r * ROW + swz<D>(r, 2 * c + hh) * 16), qf[c], st[t]);
+          dpt[t] = mfma_bf16(*(const u32x4*)(vs + r * ROW + swz<D>(r, 2 * c + hh) * 16), of[c], dpt[t]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jr = 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const int j = k0 + jr;
+          float p, grad;
+          BwdArgs const& aa = a;
+          recompute_p<MOD>(st[t][r], qi, j, slope, aa, lse2, p, grad);
+          if (cls == TILE_PARTIAL) {
+            int dj = 0;
+            if constexpr (MASK == MASK_DOCUMENT) dj = sdoc[cur][jr];
+            const bool ok = j < Skv && mask_ok<MASK>(qi, j, window, doc_i, dj);
+            p = ok ? p : 0.0f;
+          }
+          dpt[t][r] = p * (dpt[t][r] - del) * grad;
+        }
+      u32x4 sb[NT][2];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+          sb[t][cc] = u32x4{pack_bf16(dpt[t][8 * cc + 0], dpt[t][8 * cc + 1]),
+                            pack_bf16(dpt[t][8 * cc + 2], dpt[t][8 * cc + 3]),
+                            pack_bf16(dpt[t][8 * cc + 4], dpt[t][8 * cc + 5]),
+                            pack_bf16(dpt[t][8 * cc + 6], dpt[t][8 * cc + 7])};
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int ch = 4 * dt + 2 * g16 + ((gi & 3) >> 1);
+        const int half = (gi & 1) * 8;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const int r0 = 32 * t + 16 * cc + 4 * hh + (gi >> 2), r1 = r0 + 8;
+            const u32x2 lo = lds_read_tr16(ks + r0 * ROW + swz<D>(r0, ch) * 16 + half);
+            const u32x2 hi = lds_read_tr16(ks + r1 * ROW + swz<D>(r1, ch) * 16 + half);
+            dq[dt] = mfma_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, sb[t][cc], dq[dt]);
+          }
+      }
+    }
+    if (have_next) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  if (row_ok) {
+    uint16_t* dQ = (uint16_t*)a.dq + ri * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d0 = 32 * dt + 8 * rq + 4 * hh;
+        *(u32x2*)(dQ + d0) = u32x2{pack_bf16(dq[dt][4 * rq] * a.scale, dq[dt][4 * rq + 1] * a.scale),
+                                   pack_bf16(dq[dt][4 * rq + 2] * a.scale, dq[dt][4 * rq + 3] * a.scale)};
+      }
+  }
+}
+
+template <int D, int MASK, int MOD>
+static hipError_t launch_bwd_mm(const BwdArgs& a, hipStream_t st) {
+  const long rows = (long)a.B * a.Hq * a.Sq;
+  const int rows_per_block = 256 / (D / 8);
+  if (rows > 0) {
+    hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
+                       dim3(256), 0, st, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // dK, dV are written for every key (zero when no query sees it).
+  if ((long)a.B * a.Hkv * a.n_kt > 0) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK, MOD>), dim3((unsigned)(a.B * a.Hkv * a.n_kt)), dim3(256), 0,
+                       st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (rows > 0) {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, MASK, MOD>), dim3((unsigned)(a.B * a.Hq * a.n_qt)), dim3(256), 0, st,
+                       a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+template <int D, int MASK>
+static hipError_t launch_bwd_mask(const BwdArgs& a, int mod, hipStream_t st) {
+  switch (mod) {
+    case MOD_NONE: return launch_bwd_mm<D, MASK, MOD_NONE>(a, st);
+    case MOD_ALIBI: return launch_bwd_mm<D, MASK, MOD_ALIBI>(a, st);
+    case MOD_SOFTCAP: return launch_bwd_mm<D, MASK, MOD_SOFTCAP>(a, st);
+    default: return launch_bwd_mm<D, MASK, MOD_BOOST>(a, st);
+  }
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdArgs& a, int mask, int mod, hipStream_t st) {
+  switch (mask) {
+    case MASK_NONE: return launch_bwd_mask<D, MASK_NONE>(a, mod, st);
+    case MASK_CAUSAL: return launch_bwd_mask<D, MASK_CAUSAL>(a, mod, st);
+    case MASK_WINDOW: return launch_bwd_mask<D, MASK_WINDOW>(a, mod, st);
+    default: return launch_bwd_mask<D, MASK_DOCUMENT>(a, mod, st);
+  }
+}
+
+}  // namespace miattn

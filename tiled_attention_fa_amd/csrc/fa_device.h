@@ -1,0 +1,190 @@
+// Device helpers for the gfx950 attention kernels: MFMA wrappers, exp2,
+// bf16 packing, cross-half wave reductions, LDS swizzles, masks, score
+// modifiers and the workgroup-to-tile schedule.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_args.h"
+
+namespace miattn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// ---------------------------------------------------------------- MFMA
+// 32x32x16 bf16 -> fp32.  Lane l supplies A[l%32][k-slot l/32] and
+// B[k-slot l/32][l%32] (8 bf16 each); the accumulator register r of lane l
+// holds C[8(r/4) + 4(l/32) + r%4][l%32].
+__device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+// 32x32x2 fp32: one value per lane, same accumulator layout.
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Combine a value with the one in lane l ^ 32 (v_permlane32_swap).
+__device__ __forceinline__ float half_swap_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Transposing LDS read: within each 16-lane group, lane i receives element
+// i%4 of the 8-byte chunk addressed by lane 4j + i/4, for j = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_byte_ptr) {
+  typedef __attribute__((address_space(3))) bf16x4_t lds_v4;
+  const __attribute__((address_space(3))) char* p =
+      (const __attribute__((address_space(3))) char*)(lds_byte_ptr);
+  bf16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)p);
+  return __builtin_bit_cast(u32x2, t);
+}
+
+// ---------------------------------------------------------------- LDS swizzle
+// A row of D bf16 values is D/8 chunks of 16 bytes; chunk c of row r is
+// stored at chunk c ^ f(r).  Two read patterns must be bank-conflict free:
+//  * row reads (MFMA operand rows): 16 lanes read the same chunk of 16
+//    consecutive rows -> f must be a bijection on those rows;
+//  * transposing reads (lds_read_tr16): 32 lanes read 4 consecutive chunks
+//    (64 bytes) of 4 consecutive rows -> the four rows must land their
+//    64-byte groups in different quarters of the 256-byte bank window.
+// D = 128 (256-byte rows): f(r) swaps the two low 2-bit fields of r.
+// D = 64 (128-byte rows, two rows per window): f(r) = bit 1 of r moved to
+// bit 2, bits 2..3 of r in bits 0..1.
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (D == 128) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// ---------------------------------------------------------------- masks
+// Admissibility of (query i, key j), absolute indices.  `doc_i` / `doc_j`
+// are the document ids (only read for MASK_DOCUMENT).
+template <int MASK>
+__device__ __forceinline__ bool mask_ok(int i, int j, int window, int doc_i, int doc_j) {
+  if constexpr (MASK == MASK_NONE) return true;
+  if constexpr (MASK == MASK_CAUSAL) return j <= i;
+  if constexpr (MASK == MASK_WINDOW) return j <= i && i - j < window;
+  return j <= i && doc_i == doc_j;
+}
+
+// Key range [lo, hi) that can be admissible for query rows [q0, q1).
+template <int MASK>
+__device__ __forceinline__ void key_range(int q0, int q1, int Skv, int window, int& lo, int& hi) {
+  lo = 0;
+  hi = Skv;
+  if constexpr (MASK != MASK_NONE) hi = min(Skv, q1);
+  if constexpr (MASK == MASK_WINDOW) lo = max(0, q0 - window + 1);
+}
+
+// Class of the block [q0, q0+nq) x [k0, k0+nk) under an analytic mask:
+// TILE_EMPTY, TILE_PARTIAL or TILE_FULL (every pair in range and admissible).
+template <int MASK>
+__device__ __forceinline__ int block_class(int q0, int nq, int k0, int nk, int Skv, int window) {
+  const int q1 = q0 + nq - 1, k1 = k0 + nk - 1;
+  const bool in_range = k0 + nk <= Skv;
+  if constexpr (MASK == MASK_NONE) return in_range ? TILE_FULL : TILE_PARTIAL;
+  if (k0 > q1) return TILE_EMPTY;
+  if constexpr (MASK == MASK_WINDOW) {
+    if (k1 < q0 - window + 1) return TILE_EMPTY;
+    return (in_range && k1 <= q0 && q1 - k0 < window) ? TILE_FULL : TILE_PARTIAL;
+  }
+  if constexpr (MASK == MASK_CAUSAL) return (in_range && k1 <= q0) ? TILE_FULL : TILE_PARTIAL;
+  return TILE_PARTIAL;
+}
+
+// ---------------------------------------------------------------- score modifiers
+template <int MOD>
+__device__ __forceinline__ float head_slope(const ModArgs& m, int h, int Hq) {
+  if constexpr (MOD == MOD_ALIBI) {
+    if (m.slopes) return m.slopes[h];
+    return fast_exp2(-8.0f * (float)(h + 1) / (float)Hq);
+  }
+  return 0.0f;
+}
+
+// tanh from exp2: tanh(x) = 1 - 2 / (1 + 2^(2x log2 e)).
+__device__ __forceinline__ float tanh_exp2(float x) {
+  const float e = fast_exp2(2.0f * kLog2e * x);
+  return 1.0f - 2.0f * fast_rcp(1.0f + e);
+}
+
+// Modified score from the scaled score s, query i, key j.
+template <int MOD>
+__device__ __forceinline__ float apply_mod(float s, int i, int j, float slope, const ModArgs& m) {
+  if constexpr (MOD == MOD_NONE) return s;
+  if constexpr (MOD == MOD_ALIBI) return s + slope * (float)(j - i);
+  if constexpr (MOD == MOD_SOFTCAP) return m.softcap * tanh_exp2(s * m.inv_softcap);
+  int d = i - j;
+  d = d < 0 ? -d : d;
+  return d < m.boost_radius ? s * m.boost_factor : s;
+}
+
+// d(modified)/ds for the backward pass; `t` is tanh(s / softcap) for MOD_SOFTCAP.
+template <int MOD>
+__device__ __forceinline__ float mod_grad(int i, int j, float t, const ModArgs& m) {
+  if constexpr (MOD == MOD_SOFTCAP) return 1.0f - t * t;
+  if constexpr (MOD == MOD_BOOST) {
+    int d = i - j;
+    d = d < 0 ? -d : d;
+    return d < m.boost_radius ? m.boost_factor : 1.0f;
+  }
+  return 1.0f;
+}
+
+// ---------------------------------------------------------------- schedule
+// Workgroups are handed to the 8 XCDs round-robin by id.  When the number
+// of (batch, kv-head) units is a multiple of 8, every unit is pinned to one
+// XCD so its K/V stream stays in that XCD's L2, and within an XCD the tile
+// rank advances slowest so the heaviest tiles (largest index under causal
+// masks) start first.  Returns the batch, query head and tile index.
+__device__ __forceinline__ void decode_work(int P, int B, int Hq, int Hkv, int n_tiles,
+                                            bool heavy_first, int& b, int& hq, int& tile) {
+  const int G = Hq / Hkv;
+  const int NU = B * Hkv;
+  int r;
+  if ((NU & 7) == 0) {
+    const int xcd = P & 7, s = P >> 3;
+    const int per_rank = (NU >> 3) * G;
+    r = s / per_rank;
+    const int rem = s - r * per_rank;
+    const int ul = rem / G, g = rem - ul * G;
+    const int u = ul * 8 + xcd;
+    b = u / Hkv;
+    hq = (u - b * Hkv) * G + g;
+  } else {
+    const int heads = B * Hq;
+    r = P / heads;
+    const int hh = P - r * heads;
+    b = hh / Hq;
+    hq = hh - b * Hq;
+  }
+  tile = heavy_first ? (n_tiles - 1 - r) : r;
+}
+
+}  // namespace miattn

@@ -1,0 +1,21 @@
+// Host-side launchers implemented in the .hip translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "fa_args.h"
+
+namespace miattn {
+
+template <int D, bool F32>
+hipError_t launch_fwd_dt(const FwdArgs& a, int mask, int mod, hipStream_t st);
+
+template <int D>
+hipError_t launch_bwd_d(const BwdArgs& a, int mask, int mod, hipStream_t st);
+
+hipError_t launch_block_mask(int mask_kind, int window, const int32_t* doc_ids, int Sq, int Skv,
+                             const BlockMaskArgs& m, hipStream_t st);
+
+// Keys per forward step for each instantiation.
+constexpr int fwd_kv_step(bool f32) { return f32 ? 32 : 64; }
+
+}  // namespace miattn
