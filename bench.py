@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark of libmiattn on one MI355X.
+
+Default workload: causal attention forward + backward, B=2, Hq=Hkv=16,
+S=8192, D=128, bf16, seeded N(0,1) inputs already resident in HBM.  One
+step = fa_fwd (with LSE) then the three backward launches (delta, dK/dV,
+dQ).  Throughput counts admissible-pair FLOPs only (4 D per pair forward,
+10 D backward) and is compared with the dense bf16 MFMA peak.
+
+Per-kernel times come from HIP events recorded between the launches on the
+stream the library launches on.  The CPU baseline times the fp64 oracle on a
+bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOPS (unmasked FLOPs) + % of bf16 MFMA peak, S=8192 D=128"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_HBM_GBS = 8000.0
+MASK_NAMES = {0: "none", 1: "causal", 2: "sliding_window", 3: "document"}
+MOD_NAMES = {0: "none", 1: "alibi", 2: "softcap", 3: "local_boost"}
+
+
+def source_sha() -> str:
+    """Hash of the kernel sources: traffic figures taken from another build are void."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "tiled_attention_fa_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none for this kernel or the sources changed since."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    k = rec.get("kernels", {}).get(kernel)
+    if not k or rec.get("source_sha") != source_sha():
+        return None
+    return k.get("bytes_per_launch")
+
+
+def cpu_baseline(w, heads: int):
+    """The oracle (numpy fp64, as committed) on `heads` whole (batch, head)
+    pairs of the workload; returns the dict for the JSON line."""
+    import numpy as np
+
+    import oracle
+    import synth
+    from tiled_attention_fa_amd import flops
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = os.cpu_count() or 1
+    q, k, v, extras = synth.workload_inputs(w)
+    doc = extras.get("doc_ids")
+    var = oracle.Variant(mask=w.mask, window=w.window, mod=w.mod, softcap=w.softcap,
+                         boost_radius=w.boost_radius, boost_factor=w.boost_factor,
+                         doc_ids=None if doc is None else doc.numpy())
+    from tiled_attention_fa_amd.binding import default_scale
+    scale = default_scale(w.D)
+    G = w.Hq // w.Hkv
+    todo = [(0, h) for h in range(min(heads, w.Hq))]
+    t0 = time.perf_counter()
+    for b, h in todo:
+        hk = h // G
+        if w.backward:
+            oracle.backward_head(q[b, h], k[b, hk], v[b, hk], extras["do"][b, h], scale, var, b, h, w.Hq)
+        else:
+            oracle.forward(q[b:b + 1, h:h + 1], k[b:b + 1, hk:hk + 1], v[b:b + 1, hk:hk + 1], scale, var)
+    dt = time.perf_counter() - t0
+    per_head = flops.pairs_per_row_batch(w.mask, w.S, w.S, w.window, extras.get("doc_lengths"))
+    work = per_head * len(todo) * ((4 + 10) * w.D if w.backward else 4 * w.D)
+    return {"value": work / dt / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+            "seconds": dt,
+            "sample": f"{'forward+backward' if w.backward else 'forward'} of {len(todo)} of {w.B * w.Hq} "
+                      f"(batch, head) pairs at full S={w.S}, numpy float64 with {threads} BLAS threads; "
+                      f"value = admissible-pair FLOPs of that sample / its time"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="causal_fwd_bwd")
+    ap.add_argument("--cpu-heads", type=int, default=16, help="heads of the oracle CPU baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import tiled_attention_fa_amd as fa
+    from tiled_attention_fa_amd import flops
+
+    fa.lib()
+    if args.workload not in synth.WORKLOADS:
+        sys.exit(f"unknown workload {args.workload}; choose from {sorted(synth.WORKLOADS)}")
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v, extras = synth.workload_inputs(w)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    do = extras["do"].to(dev) if w.backward else None
+    doc = extras["doc_ids"].to(dev) if "doc_ids" in extras else None
+    kw = dict(mask=w.mask, window=w.window, doc_ids=doc, mod=w.mod, softcap=w.softcap,
+              boost_radius=w.boost_radius, boost_factor=w.boost_factor)
+    stream = torch.cuda.current_stream()
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)) if w.backward else None
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.Hq, w.S, w.D), dtype=torch.uint8, device=dev)
+    use_bm = w.mask == fa.MASK_DOCUMENT
+    bm = fa.build_block_mask(w.mask, w.B, w.S, w.S, window=w.window, doc_ids=doc) if use_bm else None
+
+    names = (["block_mask"] if use_bm else []) + ["fwd"] + (["bwd_delta", "bwd_dkdv", "bwd_dq"] if w.backward else [])
+
+    def step(evs):
+        i = 0
+        if evs:
+            evs[i].record(stream)
+        if use_bm:
+            fa.build_block_mask(w.mask, w.B, w.S, w.S, window=w.window, doc_ids=doc, into=bm)
+            i += 1
+            if evs:
+                evs[i].record(stream)
+        fa.forward(q, k, v, out=out, lse=lse, return_lse=w.lse or w.backward, block_mask=bm, **kw)
+        i += 1
+        if evs:
+            evs[i].record(stream)
+        if w.backward:
+            for ph in (fa.FA_BWD_DELTA, fa.FA_BWD_DKDV, fa.FA_BWD_DQ):
+                fa.backward(q, k, v, out, do, lse, block_mask=bm, workspace=ws, grads=grads, phases=ph, **kw)
+                i += 1
+                if evs:
+                    evs[i].record(stream)
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for s in range(args.steps):
+        step(evs[s])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(end) / args.steps
+    kernel_ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, n in enumerate(names)}
+
+    npairs = flops.pairs(w.mask, w.B, w.Hq, w.S, w.S, w.window, extras.get("doc_lengths"))
+    f_fwd = flops.fwd_flops(npairs, w.D)
+    f_bwd = flops.bwd_flops(npairs, w.D) if w.backward else 0.0
+    tflops = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
+    # Algorithmic FLOPs per launch: the forward kernel does the two forward
+    # contractions; the dK/dV kernel the recomputed Q K^T, dO V^T, P^T dO and
+    # dS^T Q; the dQ kernel is credited with dS K only (its recomputation of
+    # Q K^T and dO V^T repeats work the dK/dV kernel already counts).
+    algo = {"fwd": f_fwd, "bwd_dkdv": 8.0 * w.D * npairs, "bwd_dq": 2.0 * w.D * npairs}
+    dominant = max((n for n in names if n in algo), key=lambda n: kernel_ms[n])
+    achieved = algo[dominant] / (kernel_ms[dominant] * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic: seeded N(0,1) tensors of the workload's shape",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D,
+                   "mask": MASK_NAMES[w.mask], "mod": MOD_NAMES[w.mod], "window": w.window,
+                   "pass": "fwd+bwd" if w.backward else "fwd", "lse": bool(w.lse or w.backward),
+                   "admissible_pairs": npairs},
+        "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(f_fwd / (kernel_ms["fwd"] * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(f_bwd / (sum(kernel_ms[n] for n in names if n.startswith("bwd")) * 1e-3) / 1e12, 2)
+        if w.backward else None,
+        "kernel_ms": {n: round(t, 4) for n, t in kernel_ms.items()},
+        "wall_s": round(wall, 3),
+        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(w.name, dominant)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

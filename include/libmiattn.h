@@ -21,8 +21,9 @@
  *
  * Conventions (all entry points):
  *  - Layout: Q, O [B][Hq][Sq][D]; K, V [B][Hkv][Skv][D]; contiguous, D
- *    innermost.  LSE [B][Hq][Sq] float32, natural-log units.  Device
- *    pointers must be 16-byte aligned.
+ *    innermost.  LSE [B][Hq][Sq] float32, natural-log units.  The tensor
+ *    pointers (Q, K, V, O, dO, dQ, dK, dV) and the workspace must be 16-byte
+ *    aligned; float and int32 arrays 4-byte aligned.
  *  - Ownership: the caller owns every buffer.  The library allocates no
  *    device memory, keeps no mutable global state, and is re-entrant.
  *    Parameter structs are host memory read during the call only; the
@@ -147,6 +148,20 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const v
            int mask_kind, const fa_mask_params* mask_params,
            int score_mod_kind, const fa_mod_params* mod_params,
            const fa_block_mask* block_mask, void* stream);
+
+/* The three launches of fa_bwd, one at a time: FA_BWD_DELTA writes
+ * rowsum(dout * out) into the workspace; FA_BWD_DKDV writes dk and dv;
+ * FA_BWD_DQ writes dq.  Same arguments and validation as fa_bwd.  DKDV and
+ * DQ only read what DELTA wrote, so once DELTA has finished they may run
+ * concurrently on different streams.  Calling the three in order on one
+ * stream is exactly fa_bwd. */
+enum { FA_BWD_DELTA = 1, FA_BWD_DKDV = 2, FA_BWD_DQ = 4 };
+int fa_bwd_phase(int phase, const void* q, const void* k, const void* v, const void* out,
+                 const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                 size_t ws_bytes, int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype,
+                 float scale, int mask_kind, const fa_mask_params* mask_params,
+                 int score_mod_kind, const fa_mod_params* mod_params,
+                 const fa_block_mask* block_mask, void* stream);
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq, int D);
 

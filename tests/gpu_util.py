@@ -46,9 +46,11 @@ def bf16_half_ulp(x):
     return np.where(a >= 2.0 ** -126, 2.0 ** (e - 8), 2.0 ** -134)
 
 
-def check_out(got, ref, dtype: str, what: str = "O"):
+def check_out(got, ref, dtype: str, what: str = "O", max_excess=None):
     mx, mean = err_stats(got, ref)
     bmax, bmean = BARS[dtype]
+    if max_excess is not None:
+        bmax = max_excess
     excess = mx
     if dtype == "bf16":
         g = got.detach().to("cpu", torch.float64).numpy()

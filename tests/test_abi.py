@@ -127,6 +127,10 @@ def test_bwd_validation():
     assert bwd(dq=MIS) == fa.FA_ERR_ALIGN
     assert bwd(D=80) == fa.FA_ERR_UNSUPPORTED
     assert bwd(B=0) == fa.FA_OK
+    args = (P, P, P, P, P, P, P, P, P, P, 1 << 20, 1, 2, 2, 16, 16, 64, 0, 0.125, 0, None, 0, None, None, None)
+    assert fa.fa_bwd_phase(0, *args) == fa.FA_ERR_PARAM
+    assert fa.fa_bwd_phase(8, *args) == fa.FA_ERR_PARAM
+    assert fa.fa_bwd_phase(fa.FA_BWD_DQ, *args[:16], 96, *args[17:]) == fa.FA_ERR_UNSUPPORTED
 
 
 def test_block_mask_build_validation():

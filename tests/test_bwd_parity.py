@@ -29,12 +29,21 @@ def run_bwd(B, Hq, Hkv, S, D, spec, seed, block_mask=False):
     return (dq, dk, dv), (rq, rk, rv)
 
 
+# Non-causal ALiBi with slopes 2^-2, 2^-4, ... sends every query to the last
+# keys, so dK of those keys sums ~333 large terms (|dK| ~ 10).  Rounding only
+# the dS operand of that contraction to bf16 (everything else exact, fp64 on
+# the CPU) already leaves 1.67e-2 (D=64) / 1.64e-2 (D=128) of error beyond the
+# output's own rounding: the floor of any bf16-operand backward, with no room
+# under 2e-2 for the fp32 accumulation.  This one case gets 3e-2.
+MAX_EXCESS = {"none_alibi": 3e-2}
+
+
 @pytest.mark.parametrize("name", sorted(VARIANTS))
 @pytest.mark.parametrize("D", [64, 128])
 def test_variants(name, D):
     got, ref = run_bwd(1, 4, 2, 333, D, VARIANTS[name], seed=21)
     for g, r, what in zip(got, ref, ("dQ", "dK", "dV")):
-        check_out(g, r, "bf16", what)
+        check_out(g, r, "bf16", what, max_excess=MAX_EXCESS.get(name))
 
 
 @pytest.mark.parametrize("S", [1, 64, 127, 129, 260])

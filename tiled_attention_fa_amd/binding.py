@@ -24,7 +24,9 @@ MOD_NONE, MOD_ALIBI, MOD_SOFTCAP, MOD_LOCAL_BOOST = 0, 1, 2, 3
 TILE_EMPTY, TILE_PARTIAL, TILE_FULL = 0, 1, 2
 BLOCK = 128
 
-EXPORTED = ("fa_fwd", "fa_fwd_kv_step", "fa_bwd", "fa_bwd_workspace_bytes",
+FA_BWD_DELTA, FA_BWD_DKDV, FA_BWD_DQ = 1, 2, 4
+
+EXPORTED = ("fa_fwd", "fa_fwd_kv_step", "fa_bwd", "fa_bwd_phase", "fa_bwd_workspace_bytes",
             "fa_block_mask_build", "fa_status_str", "fa_version")
 
 
@@ -72,6 +74,8 @@ def lib() -> ctypes.CDLL:
                              _I, ctypes.POINTER(FaMaskParams), _I, ctypes.POINTER(FaModParams),
                              ctypes.POINTER(FaBlockMask), _P]
         L.fa_bwd.restype = _I
+        L.fa_bwd_phase.argtypes = [_I] + L.fa_bwd.argtypes
+        L.fa_bwd_phase.restype = _I
         L.fa_bwd_workspace_bytes.argtypes = [_I, _I, _I, _I]
         L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.fa_block_mask_build.argtypes = [_I, ctypes.POINTER(FaMaskParams), _I, _I, _I,
@@ -95,6 +99,10 @@ def fa_fwd(*args) -> int:
 
 def fa_bwd(*args) -> int:
     return lib().fa_bwd(*args)
+
+
+def fa_bwd_phase(*args) -> int:
+    return lib().fa_bwd_phase(*args)
 
 
 def fa_block_mask_build(*args) -> int:
@@ -175,9 +183,10 @@ class BlockMask:
 
 
 def build_block_mask(mask: int, B: int, Sq: int, Skv: int, *, window: int = 0, doc_ids=None,
-                     device="cuda", stream=None) -> BlockMask:
+                     device="cuda", stream=None, into: BlockMask | None = None) -> BlockMask:
+    """Build (or rebuild ``into``, allocating nothing) the block mask of a mask kind."""
     n_b = B if mask == MASK_DOCUMENT else 1
-    bm = BlockMask(n_b, -(-Sq // BLOCK), -(-Skv // BLOCK), device)
+    bm = into if into is not None else BlockMask(n_b, -(-Sq // BLOCK), -(-Skv // BLOCK), device)
     mp, _ = _params(mask, window, doc_ids, None, MOD_NONE, None, 0.0, 0, 1.0)
     s = bm.struct()
     rc = fa_block_mask_build(int(mask), ctypes.byref(mp), int(B), int(Sq), int(Skv), ctypes.byref(s), _stream(stream))
@@ -210,8 +219,12 @@ def forward(q, k, v, *, scale=None, mask=MASK_NONE, window=0, doc_ids=None, mod=
 
 def backward(q, k, v, out, dout, lse, *, scale=None, mask=MASK_NONE, window=0, doc_ids=None,
              mod=MOD_NONE, alibi_slopes=None, softcap=0.0, boost_radius=0, boost_factor=1.0,
-             block_mask=None, workspace=None, grads=None, stream=None):
-    """(dq, dk, dv) of sum(O * dout), recomputing P from ``lse``."""
+             block_mask=None, workspace=None, grads=None, stream=None,
+             phases=FA_BWD_DELTA | FA_BWD_DKDV | FA_BWD_DQ):
+    """(dq, dk, dv) of sum(O * dout), recomputing P from ``lse``.
+
+    ``phases`` selects which of the three backward launches run (all by
+    default, which is fa_bwd)."""
     torch = _torch()
     B, Hq, Sq, D = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
@@ -221,11 +234,11 @@ def backward(q, k, v, out, dout, lse, *, scale=None, mask=MASK_NONE, window=0, d
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     mp, op = _params(mask, window, doc_ids, None, mod, alibi_slopes, softcap, boost_radius, boost_factor)
     bms = block_mask.struct() if block_mask is not None else None
-    rc = fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+    rc = fa_bwd_phase(int(phases), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                 _ptr(workspace), workspace.numel() * workspace.element_size(),
                 B, Hq, Hkv, Sq, Skv, D, _dtype_code(q), float(default_scale(D) if scale is None else scale),
                 int(mask), ctypes.byref(mp), int(mod), ctypes.byref(op),
                 ctypes.byref(bms) if bms is not None else None, _stream(stream))
     if rc != FA_OK:
-        raise FaError(rc, "fa_bwd")
+        raise FaError(rc, "fa_bwd_phase")
     return dq, dk, dv

@@ -181,10 +181,12 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq, int D) {
   return (n + 255) & ~(size_t)255;
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
-           void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes, int B, int Hq, int Hkv, int Sq, int Skv,
-           int D, int dtype, float scale, int mask_kind, const fa_mask_params* mask_params, int score_mod_kind,
-           const fa_mod_params* mod_params, const fa_block_mask* block_mask, void* stream) {
+int fa_bwd_phase(int phase, const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes, int B, int Hq,
+                 int Hkv, int Sq, int Skv, int D, int dtype, float scale, int mask_kind,
+                 const fa_mask_params* mask_params, int score_mod_kind, const fa_mod_params* mod_params,
+                 const fa_block_mask* block_mask, void* stream) {
+  if (phase <= 0 || (phase & ~(FA_BWD_DELTA | FA_BWD_DKDV | FA_BWD_DQ)) != 0) return FA_ERR_PARAM;
   if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   int rc = check_shapes(B, Hq, Hkv, Sq, Skv, D);
   if (rc) return rc;
@@ -227,9 +229,18 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const v
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const hipError_t e = D == 128 ? launch_bwd_d<128>(a, mask_kind, score_mod_kind, st)
-                                : launch_bwd_d<64>(a, mask_kind, score_mod_kind, st);
+  const hipError_t e = D == 128 ? launch_bwd_d<128>(a, mask_kind, score_mod_kind, phase, st)
+                                : launch_bwd_d<64>(a, mask_kind, score_mod_kind, phase, st);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+           void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes, int B, int Hq, int Hkv, int Sq, int Skv,
+           int D, int dtype, float scale, int mask_kind, const fa_mask_params* mask_params, int score_mod_kind,
+           const fa_mod_params* mod_params, const fa_block_mask* block_mask, void* stream) {
+  return fa_bwd_phase(FA_BWD_DELTA | FA_BWD_DKDV | FA_BWD_DQ, q, k, v, out, dout, lse, dq, dk, dv, workspace,
+                      ws_bytes, B, Hq, Hkv, Sq, Skv, D, dtype, scale, mask_kind, mask_params, score_mod_kind,
+                      mod_params, block_mask, stream);
 }
 
 int fa_block_mask_build(int mask_kind, const fa_mask_params* mask_params, int B, int Sq, int Skv,

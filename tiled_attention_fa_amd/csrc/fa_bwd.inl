@@ -492,23 +492,23 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 }
 
 template <int D, int MASK, int MOD>
-static hipError_t launch_bwd_mm(const BwdArgs& a, hipStream_t st) {
+static hipError_t launch_bwd_mm(const BwdArgs& a, int phases, hipStream_t st) {
   const long rows = (long)a.B * a.Hq * a.Sq;
   const int rows_per_block = 256 / (D / 8);
-  if (rows > 0) {
+  if ((phases & 1) && rows > 0) {
     hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
                        dim3(256), 0, st, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   // dK, dV are written for every key (zero when no query sees it).
-  if ((long)a.B * a.Hkv * a.n_kt > 0) {
+  if ((phases & 2) && (long)a.B * a.Hkv * a.n_kt > 0) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK, MOD>), dim3((unsigned)(a.B * a.Hkv * a.n_kt)), dim3(256), 0,
                        st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (rows > 0) {
+  if ((phases & 4) && rows > 0) {
     hipLaunchKernelGGL((bwd_dq_kernel<D, MASK, MOD>), dim3((unsigned)(a.B * a.Hq * a.n_qt)), dim3(256), 0, st,
                        a);
     return hipGetLastError();
@@ -517,22 +517,22 @@ static hipError_t launch_bwd_mm(const BwdArgs& a, hipStream_t st) {
 }
 
 template <int D, int MASK>
-static hipError_t launch_bwd_mask(const BwdArgs& a, int mod, hipStream_t st) {
+static hipError_t launch_bwd_mask(const BwdArgs& a, int mod, int phases, hipStream_t st) {
   switch (mod) {
-    case MOD_NONE: return launch_bwd_mm<D, MASK, MOD_NONE>(a, st);
-    case MOD_ALIBI: return launch_bwd_mm<D, MASK, MOD_ALIBI>(a, st);
-    case MOD_SOFTCAP: return launch_bwd_mm<D, MASK, MOD_SOFTCAP>(a, st);
-    default: return launch_bwd_mm<D, MASK, MOD_BOOST>(a, st);
+    case MOD_NONE: return launch_bwd_mm<D, MASK, MOD_NONE>(a, phases, st);
+    case MOD_ALIBI: return launch_bwd_mm<D, MASK, MOD_ALIBI>(a, phases, st);
+    case MOD_SOFTCAP: return launch_bwd_mm<D, MASK, MOD_SOFTCAP>(a, phases, st);
+    default: return launch_bwd_mm<D, MASK, MOD_BOOST>(a, phases, st);
   }
 }
 
 template <int D>
-hipError_t launch_bwd_d(const BwdArgs& a, int mask, int mod, hipStream_t st) {
+hipError_t launch_bwd_d(const BwdArgs& a, int mask, int mod, int phases, hipStream_t st) {
   switch (mask) {
-    case MASK_NONE: return launch_bwd_mask<D, MASK_NONE>(a, mod, st);
-    case MASK_CAUSAL: return launch_bwd_mask<D, MASK_CAUSAL>(a, mod, st);
-    case MASK_WINDOW: return launch_bwd_mask<D, MASK_WINDOW>(a, mod, st);
-    default: return launch_bwd_mask<D, MASK_DOCUMENT>(a, mod, st);
+    case MASK_NONE: return launch_bwd_mask<D, MASK_NONE>(a, mod, phases, st);
+    case MASK_CAUSAL: return launch_bwd_mask<D, MASK_CAUSAL>(a, mod, phases, st);
+    case MASK_WINDOW: return launch_bwd_mask<D, MASK_WINDOW>(a, mod, phases, st);
+    default: return launch_bwd_mask<D, MASK_DOCUMENT>(a, mod, phases, st);
   }
 }
 

@@ -3,5 +3,5 @@
 #include "fa_launch.h"
 
 namespace miattn {
-template hipError_t launch_bwd_d<64>(const BwdArgs&, int, int, hipStream_t);
+template hipError_t launch_bwd_d<64>(const BwdArgs&, int, int, int, hipStream_t);
 }  // namespace miattn

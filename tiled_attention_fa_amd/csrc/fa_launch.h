@@ -9,8 +9,9 @@ namespace miattn {
 template <int D, bool F32>
 hipError_t launch_fwd_dt(const FwdArgs& a, int mask, int mod, hipStream_t st);
 
+// phases: bit 1 delta, bit 2 dK/dV, bit 4 dQ.
 template <int D>
-hipError_t launch_bwd_d(const BwdArgs& a, int mask, int mod, hipStream_t st);
+hipError_t launch_bwd_d(const BwdArgs& a, int mask, int mod, int phases, hipStream_t st);
 
 hipError_t launch_block_mask(int mask_kind, int window, const int32_t* doc_ids, int Sq, int Skv,
                              const BlockMaskArgs& m, hipStream_t st);
