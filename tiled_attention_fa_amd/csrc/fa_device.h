@@ -82,6 +82,44 @@ __device__ __forceinline__ int swz(int r, int c) {
   return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
+// ---------------------------------------------------------------- global -> LDS
+// Buffer resource over `bytes` bytes at `base` (raw buffer, no stride): loads
+// at offsets >= bytes return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Copy rows [r0, r0 + ROWS) of a bf16 [rows][D] matrix into an LDS tile in
+// the swizzled layout, straight from memory to LDS (buffer_load ... lds, no
+// registers).  Each load instruction fills 1 KB of the tile, lane l writing
+// bytes 16 l .. 16 l + 15, so lane l fetches the global chunk that the
+// swizzle places there.  Rows past the end of the buffer read as zeros.
+// All 4 waves of the workgroup call it; each issues ROWS * D / 2048 loads.
+template <int D, int ROWS>
+__device__ __forceinline__ void tile_to_lds(__amdgpu_buffer_rsrc_t rsrc, int r0, char* tile, int wave, int lane) {
+  constexpr int ROW = D * 2, PER_WAVE = ROWS * ROW / 1024 / 4;
+  static_assert(PER_WAVE * 4 * 1024 == ROWS * ROW, "tile must split into 1 KB loads over 4 waves");
+  const int w = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int kb = w * PER_WAVE + i;
+    const int byte = kb * 1024 + lane * 16;
+    const int r = byte / ROW, p = (byte % ROW) / 16;
+    const uint32_t off = (uint32_t)(((r0 + r) * D + swz<D>(r, p) * 8) * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(tile + kb * 1024), 16,
+                                              off, 0, 0, 0);
+  }
+}
+
+// 64 int32 values (e.g. document ids of a key tile) into LDS by one wave.
+__device__ __forceinline__ void ints_to_lds(__amdgpu_buffer_rsrc_t rsrc, int i0, int* dst, int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)dst, 4,
+                                            (uint32_t)((i0 + lane) * 4), 0, 0, 0);
+}
+
+// Wait until every load this wave issued has landed (vmcnt = 0).
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
+
 // ---------------------------------------------------------------- masks
 // Admissibility of (query i, key j), absolute indices.  `doc_i` / `doc_j`
 // are the document ids (only read for MASK_DOCUMENT).

@@ -12,9 +12,9 @@
 // tile), each wave owning 32 query rows; the key/value tiles are shared
 // through LDS ("FlashAttention-2" page, §3-§4: query blocks spread over the
 // warps, key/value blocks traversed together).  Per key step of 64 keys:
-//   1. K and V tiles (64 x D bf16) stream from HBM into one of two LDS
-//      stages with 16-byte loads; the next step's loads are in flight while
-//      the current step computes.
+//   1. K and V tiles (64 x D bf16) stream from HBM straight into one of two
+//      LDS stages (buffer loads to LDS, zero-filled past the last key); the
+//      next step's loads are in flight while the current step computes.
 //   2. S^T = K Q^T on 32x32x16 bf16 MFMA: each lane owns one query column,
 //      so the row max and row sum are in-lane plus one v_permlane32_swap.
 //   3. scores -> modifier -> mask (only on partial tiles) -> exp2 domain.
@@ -37,12 +37,10 @@ template <int D, bool F32>
 struct FwdSmem {
   static constexpr int ROW = F32 ? (D + 1) * 4 : D * 2;  // bytes per LDS row
   static constexpr int TILE = FwdCfg<F32>::BN * ROW;     // one K or V tile
-  static constexpr int STAGES = F32 ? 1 : 2;
-  static constexpr int BYTES = STAGES * 2 * TILE;
 };
 
-template <int D, bool F32, int MASK, int MOD>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
+template <int D, bool F32, int MASK, int MOD, bool BM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(FwdArgs a) {
   using Cfg = FwdCfg<F32>;
   using Sm = FwdSmem<D, F32>;
   constexpr int BN = Cfg::BN, NT = Cfg::NT;
@@ -50,11 +48,14 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   constexpr int DT = D / 32;                 // 32-row d tiles of O^T
   constexpr int KC = F32 ? D / 2 : D / 16;   // MFMA k-chunks of the S product
   constexpr int NCH = F32 ? D / 4 : D / 8;   // 16-byte chunks per global row
-  constexpr int LOADS = BN * NCH / 256;      // 16-byte chunks per thread per tensor
+  constexpr int LOADS = BN * NCH / 256;      // 16-byte chunks per thread per tensor (fp32 path)
   static_assert(LOADS * 256 == BN * NCH, "tile load must divide evenly");
 
-  __shared__ __attribute__((aligned(16))) char smem[Sm::BYTES];
-  __shared__ int sdoc[Sm::STAGES][BN];
+  // Two LDS stages as separate objects: the step reading one stage never
+  // waits on the loads in flight into the other.
+  __shared__ __attribute__((aligned(16))) char sK0[TILE], sV0[TILE];
+  __shared__ __attribute__((aligned(16))) char sK1[F32 ? 16 : TILE], sV1[F32 ? 16 : TILE];
+  __shared__ __attribute__((aligned(16))) int sD0[BN], sD1[BN];
 
   int b, hq, qt;
   decode_work(blockIdx.x, a.B, a.Hq, a.Hkv, a.n_qt, MASK == MASK_CAUSAL || MASK == MASK_DOCUMENT, b,
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
 
   // ---- key steps: analytic range, or the block mask's list of non-empty blocks
   constexpr int STEPS_PER_BLOCK = kMaskBlock / BN;
-  const bool use_bm = a.bm.tile_state != nullptr;
+  constexpr bool use_bm = BM;
   int step_lo = 0, n_steps = 0;
   const int32_t* bm_list = nullptr;
   const uint8_t* bm_state = nullptr;
@@ -113,51 +114,60 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
       n_steps = (hi + BN - 1) / BN - step_lo;
     }
   }
-  auto step_k0 = [&](int s) -> int {
-    if (use_bm) return bm_list[s / STEPS_PER_BLOCK] * kMaskBlock + (s % STEPS_PER_BLOCK) * BN;
-    return (step_lo + s) * BN;
+  // Block-mask path: list entry (block index) of step s.  Analytic path:
+  // the first key of step s.
+  auto fetch_blk = [&](int s) -> int {
+    if (s >= n_steps) return 0;
+    if constexpr (BM) return bm_list[s / STEPS_PER_BLOCK];
+    return step_lo + s;
+  };
+  auto key0 = [&](int s, int blk) -> int {
+    if constexpr (BM) return blk * kMaskBlock + (s % STEPS_PER_BLOCK) * BN;
+    return blk * BN;
   };
 
-  // ---- global -> register staging of one K/V tile
-  u32x4 kr[LOADS], vr[LOADS];
-  int dr = -1;
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int p = 0; p < LOADS; ++p) {
-      const int id = tid + 256 * p, r = id / NCH, c = id % NCH, j = k0 + r;
-      if (j < Skv) {
-        kr[p] = *(const u32x4*)((const char*)K + ((size_t)j * D) * sizeof(elem_t) + c * 16);
-        vr[p] = *(const u32x4*)((const char*)V + ((size_t)j * D) * sizeof(elem_t) + c * 16);
-      } else {
-        kr[p] = u32x4{0, 0, 0, 0};
-        vr[p] = u32x4{0, 0, 0, 0};
+  // ---- tile loads.  bf16: straight from memory into an LDS stage (buffer
+  // loads, zero past Skv).  fp32: through registers into the single stage.
+  __amdgpu_buffer_rsrc_t rsK = make_rsrc(K, (uint32_t)Skv * D * (uint32_t)sizeof(elem_t));
+  __amdgpu_buffer_rsrc_t rsV = make_rsrc(V, (uint32_t)Skv * D * (uint32_t)sizeof(elem_t));
+  __amdgpu_buffer_rsrc_t rsD = make_rsrc(doc, MASK == MASK_DOCUMENT ? (uint32_t)Skv * 4 : 0u);
+  auto issue = [&](int k0, char* ks, char* vs, int* ds) {
+    if constexpr (!F32) {
+      tile_to_lds<D, BN>(rsK, k0, ks, wave, lane);
+      tile_to_lds<D, BN>(rsV, k0, vs, wave, lane);
+      if constexpr (MASK == MASK_DOCUMENT) {
+        if (wave == 0) ints_to_lds(rsD, k0, ds, lane);
       }
     }
-    if constexpr (MASK == MASK_DOCUMENT) {
-      if (tid < BN) dr = (k0 + tid < Skv) ? doc[k0 + tid] : -2;
-    }
   };
-  auto lstore = [&](int stage) {
-    char* ks = smem + stage * 2 * TILE;
-    char* vs = ks + TILE;
+  auto load_f32 = [&](int k0) {
+    if constexpr (F32) {
+      u32x4 kr[LOADS], vr[LOADS];
+      int dr = -1;
 #pragma unroll
-    for (int p = 0; p < LOADS; ++p) {
-      const int id = tid + 256 * p, r = id / NCH, c = id % NCH;
-      if constexpr (F32) {
-        float* kd = (float*)(ks + r * ROW) + 4 * c;
-        float* vd = (float*)(vs + r * ROW) + 4 * c;
+      for (int p = 0; p < LOADS; ++p) {
+        const int id = tid + 256 * p, r = id / NCH, c = id % NCH, j = k0 + r;
+        const bool ok = j < Skv;
+        kr[p] = ok ? *(const u32x4*)((const float*)K + (size_t)j * D + 4 * c) : u32x4{0, 0, 0, 0};
+        vr[p] = ok ? *(const u32x4*)((const float*)V + (size_t)j * D + 4 * c) : u32x4{0, 0, 0, 0};
+      }
+      if constexpr (MASK == MASK_DOCUMENT) {
+        if (tid < BN) dr = (k0 + tid < Skv) ? doc[k0 + tid] : -2;
+      }
+#pragma unroll
+      for (int p = 0; p < LOADS; ++p) {
+        const int id = tid + 256 * p, r = id / NCH, c = id % NCH;
+        float* kd = (float*)(sK0 + r * ROW) + 4 * c;
+        float* vd = (float*)(sV0 + r * ROW) + 4 * c;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           kd[e] = __uint_as_float(kr[p][e]);
           vd[e] = __uint_as_float(vr[p][e]);
         }
-      } else {
-        *(u32x4*)(ks + r * ROW + swz<D>(r, c) * 16) = kr[p];
-        *(u32x4*)(vs + r * ROW + swz<D>(r, c) * 16) = vr[p];
       }
-    }
-    if constexpr (MASK == MASK_DOCUMENT) {
-      if (tid < BN) sdoc[stage][tid] = dr;
+      if constexpr (MASK == MASK_DOCUMENT) {
+        if (tid < BN) sD0[tid] = dr;
+      }
     }
   };
 
@@ -165,33 +175,31 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   f32x16 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
-
   int visited = 0;
-  if (n_steps > 0) {
-    gload(step_k0(0));
-    lstore(0);
-  }
-  __syncthreads();
 
-  for (int s = 0; s < n_steps; ++s) {
-    const int cur = F32 ? 0 : (s & 1);
-    const int k0 = step_k0(s);
+  // One key step on the stage (ks, vs, ds); the next step's tiles go to
+  // (kn, vn, dn).  The block index of this step and the next, and the block
+  // state of this step, are in registers.  Block-mask reads for later steps
+  // (list entry two steps ahead, state one step ahead) are issued after the
+  // tile loads and only consumed in the next step, after its wait.
+  int blk_c = 0, blk_n = 0, st_c = 0, st_n = 0;
+  auto step = [&](int s, const char* ks, const char* vs, const int* ds, char* kn, char* vn, int* dn) {
+    const int k0 = key0(s, blk_c);
     const bool have_next = s + 1 < n_steps;
-    if (!F32 && have_next) gload(step_k0(s + 1));
+    if (have_next) issue(key0(s + 1, blk_n), kn, vn, dn);
+    const int blk_nn = fetch_blk(s + 2);
+    if constexpr (BM) st_n = have_next ? bm_state[blk_n] : 0;
     if (k0 < Skv) ++visited;
 
     int cls;
-    if (use_bm) {
-      cls = (k0 >= Skv) ? TILE_EMPTY
-                        : (bm_state[bm_list[s / STEPS_PER_BLOCK]] == TILE_FULL ? TILE_FULL : TILE_PARTIAL);
+    if constexpr (BM) {
+      cls = (k0 >= Skv) ? TILE_EMPTY : (st_c == TILE_FULL ? TILE_FULL : TILE_PARTIAL);
     } else {
       cls = block_class<MASK>(qw0, 32, k0, BN, Skv, window);
     }
     if (qw0 >= Sq) cls = TILE_EMPTY;
 
     if (cls != TILE_EMPTY) {
-      const char* ks = smem + cur * 2 * TILE;
-      const char* vs = ks + TILE;
       // ---- S^T = K Q^T  (lane: query column qi; register r: key 8(r/4) + 4hh + r%4)
       f32x16 st[NT];
 #pragma unroll
@@ -232,7 +240,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
             }
             if (cls == TILE_PARTIAL) {
               int dj = 0;
-              if constexpr (MASK == MASK_DOCUMENT) dj = sdoc[cur][jr];
+              if constexpr (MASK == MASK_DOCUMENT) dj = ds[jr];
               const bool ok = j < Skv && mask_ok<MASK>(qi, j, window, doc_i, dj);
               x = ok ? x : kNegInf;
             }
@@ -303,16 +311,37 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
       }
     }
 
-    if (F32) {
+    if constexpr (F32) {
       __syncthreads();
-      if (have_next) {
-        gload(step_k0(s + 1));
-        lstore(0);
-      }
+      if (have_next) load_f32(key0(s + 1, blk_n));
       __syncthreads();
     } else {
-      if (have_next) lstore(cur ^ 1);
+      wait_loads();
       __syncthreads();
+    }
+    blk_c = blk_n;
+    st_c = st_n;
+    blk_n = blk_nn;
+  };
+
+  blk_c = fetch_blk(0);
+  blk_n = fetch_blk(1);
+  if constexpr (BM) st_c = n_steps > 0 ? bm_state[blk_c] : 0;
+  if (n_steps > 0) {
+    if constexpr (F32) {
+      load_f32(key0(0, blk_c));
+    } else {
+      issue(key0(0, blk_c), sK0, sV0, sD0);
+      wait_loads();
+    }
+  }
+  __syncthreads();
+  if constexpr (F32) {
+    for (int s = 0; s < n_steps; ++s) step(s, sK0, sV0, sD0, sK0, sV0, sD0);
+  } else {
+    for (int s = 0; s < n_steps; s += 2) {
+      step(s, sK0, sV0, sD0, sK1, sV1, sD1);
+      if (s + 1 < n_steps) step(s + 1, sK1, sV1, sD1, sK0, sV0, sD0);
     }
   }
 
@@ -340,25 +369,31 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   if (a.visited != nullptr && tid == 0) atomicAdd(&a.visited[(size_t)(b * a.Hq + hq) * a.n_qt + qt], visited);
 }
 
-template <int D, bool F32, int MASK>
+template <int D, bool F32, int MASK, bool BM>
 static hipError_t launch_mod(const FwdArgs& a, int mod, hipStream_t st) {
   const dim3 grid((unsigned)(a.B * a.Hq * a.n_qt)), block(256);
   switch (mod) {
-    case MOD_NONE: hipLaunchKernelGGL((fwd_kernel<D, F32, MASK, MOD_NONE>), grid, block, 0, st, a); break;
-    case MOD_ALIBI: hipLaunchKernelGGL((fwd_kernel<D, F32, MASK, MOD_ALIBI>), grid, block, 0, st, a); break;
-    case MOD_SOFTCAP: hipLaunchKernelGGL((fwd_kernel<D, F32, MASK, MOD_SOFTCAP>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((fwd_kernel<D, F32, MASK, MOD_BOOST>), grid, block, 0, st, a); break;
+    case MOD_NONE: hipLaunchKernelGGL((fwd_kernel<D, F32, MASK, MOD_NONE, BM>), grid, block, 0, st, a); break;
+    case MOD_ALIBI: hipLaunchKernelGGL((fwd_kernel<D, F32, MASK, MOD_ALIBI, BM>), grid, block, 0, st, a); break;
+    case MOD_SOFTCAP: hipLaunchKernelGGL((fwd_kernel<D, F32, MASK, MOD_SOFTCAP, BM>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((fwd_kernel<D, F32, MASK, MOD_BOOST, BM>), grid, block, 0, st, a); break;
   }
   return hipGetLastError();
+}
+
+template <int D, bool F32, int MASK>
+static hipError_t launch_bm(const FwdArgs& a, int mod, hipStream_t st) {
+  return a.bm.tile_state != nullptr ? launch_mod<D, F32, MASK, true>(a, mod, st)
+                                    : launch_mod<D, F32, MASK, false>(a, mod, st);
 }
 
 template <int D, bool F32>
 hipError_t launch_fwd_dt(const FwdArgs& a, int mask, int mod, hipStream_t st) {
   switch (mask) {
-    case MASK_NONE: return launch_mod<D, F32, MASK_NONE>(a, mod, st);
-    case MASK_CAUSAL: return launch_mod<D, F32, MASK_CAUSAL>(a, mod, st);
-    case MASK_WINDOW: return launch_mod<D, F32, MASK_WINDOW>(a, mod, st);
-    default: return launch_mod<D, F32, MASK_DOCUMENT>(a, mod, st);
+    case MASK_NONE: return launch_bm<D, F32, MASK_NONE>(a, mod, st);
+    case MASK_CAUSAL: return launch_bm<D, F32, MASK_CAUSAL>(a, mod, st);
+    case MASK_WINDOW: return launch_bm<D, F32, MASK_WINDOW>(a, mod, st);
+    default: return launch_bm<D, F32, MASK_DOCUMENT>(a, mod, st);
   }
 }
 
