@@ -140,7 +140,8 @@ int fa_fwd_kv_step(int D, int dtype);
  * and dk, dv [B][Hkv][Skv][D] (summed over each GQA group), accumulating in
  * float32 and rounding once.  workspace: device, at least
  * fa_bwd_workspace_bytes(B, Hq, Sq, D) bytes, 16-byte aligned, contents
- * need not be initialised.  Supported: dtype FA_BF16, D in {64, 128}, every
+ * need not be initialised (it receives two [B][Hq][Sq] float arrays: the
+ * row sums of dout * out and the LSE in log2 units).  Supported: dtype FA_BF16, D in {64, 128}, every
  * mask and modifier. */
 int fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,

@@ -48,8 +48,9 @@ def test_host_helpers():
     assert fa.fa_fwd_kv_step(128, fa.FA_BF16) == 64
     assert fa.fa_fwd_kv_step(64, fa.FA_F32) == 32
     assert fa.fa_fwd_kv_step(96, fa.FA_BF16) == fa.FA_ERR_UNSUPPORTED
-    assert fa.fa_bwd_workspace_bytes(2, 16, 8192, 128) == 2 * 16 * 8192 * 4
-    assert fa.fa_bwd_workspace_bytes(1, 1, 3, 64) == 256
+    assert fa.fa_bwd_workspace_bytes(2, 16, 8192, 128) == 2 * (2 * 16 * 8192 * 4)
+    assert fa.fa_bwd_workspace_bytes(1, 1, 10, 64) == 2 * 256
+    assert fa.fa_bwd_workspace_bytes(0, 1, 3, 64) == 256
 
 
 P = ctypes.c_void_p(0x100000)      # never dereferenced: every call below fails validation

@@ -174,11 +174,17 @@ int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, i
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// Workspace: two [B][Hq][Sq] float arrays (row sums of dO * O, and LSE in
+// log2 units), each starting on a 256-byte boundary.
+static size_t ws_half(int B, int Hq, int Sq) {
+  const size_t n = (size_t)B * Hq * Sq * sizeof(float);
+  return (n + 255) & ~(size_t)255;
+}
+
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq, int D) {
   (void)D;
   if (B <= 0 || Hq <= 0 || Sq <= 0) return 256;
-  const size_t n = (size_t)B * Hq * Sq * sizeof(float);
-  return (n + 255) & ~(size_t)255;
+  return 2 * ws_half(B, Hq, Sq);
 }
 
 int fa_bwd_phase(int phase, const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -215,6 +221,7 @@ int fa_bwd_phase(int phase, const void* q, const void* k, const void* v, const v
   a.dout = dout;
   a.lse = lse;
   a.delta = (float*)workspace;
+  a.lse2 = (const float*)((char*)workspace + ws_half(B, Hq, Sq));
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;

@@ -56,7 +56,8 @@ struct BwdArgs {
   const void* o;
   const void* dout;
   const float* lse;
-  float* delta;  // [B][Hq][Sq] workspace: rowsum(dO * O)
+  float* delta;       // [B][Hq][Sq] workspace: rowsum(dO * O)
+  const float* lse2;  // [B][Hq][Sq] workspace: LSE * log2(e), +inf for empty rows
   void* dq;
   void* dk;
   void* dv;

@@ -7,20 +7,25 @@
 //   P = exp(mod(scale q.k) - LSE), dV = P^T dO, dP = dO V^T,
 //   delta_i = rowsum(dO_i * O_i), dS = P (dP - delta) mod',
 //   dQ = scale dS K, dK = scale dS^T Q.
-// Three launches on one stream: delta, then a key-stationary kernel that
-// owns 128 keys and loops over every query head of its GQA group and every
-// query step (dK, dV accumulated in registers, written once), then a
-// query-stationary kernel for dQ (like the forward pass).  Nothing is
-// accumulated with atomics, so the results are deterministic.
+// Three launches on one stream: the row pass (delta and LSE in log2 units),
+// then a key-stationary kernel that owns 128 keys and loops over every query
+// head of its GQA group and every query step (dK, dV accumulated in
+// registers, written once), then a query-stationary kernel for dQ (like the
+// forward pass).  Nothing is accumulated with atomics, so the results are
+// deterministic.  Q/dO (resp. K/V) tiles go straight from memory into
+// per-stage LDS objects, with the step loop unrolled by two.
 #include "fa_device.h"
 
 namespace miattn {
 
-// ---------------------------------------------------------------- delta
+// ---------------------------------------------------------------- row pass
+// delta[row] = rowsum(dO * O); lse2[row] = LSE * log2(e), or +inf for rows
+// with no admissible key (their probabilities are all zero).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restrict__ o,
                                                         const uint16_t* __restrict__ dout,
-                                                        float* __restrict__ delta, long rows) {
+                                                        const float* __restrict__ lse, float* __restrict__ delta,
+                                                        float* __restrict__ lse2, long rows) {
   constexpr int LPR = D / 8;  // lanes per row, 16 bytes each
   const long row = (long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
   const int c = threadIdx.x % LPR;
@@ -33,7 +38,11 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
   }
 #pragma unroll
   for (int w = LPR / 2; w >= 1; w >>= 1) s += __shfl_xor(s, w, LPR);
-  if (row < rows && c == 0) delta[row] = s;
+  if (row < rows && c == 0) {
+    delta[row] = s;
+    const float L = lse[row];
+    lse2[row] = (L == kNegInf) ? __builtin_inff() : L * kLog2e;
+  }
 }
 
 // Probability, and the factor that turns dP - delta into dS, for one
@@ -60,22 +69,25 @@ __device__ __forceinline__ void recompute_p(float sraw, int i, int j, float slop
   p = fast_exp2(x2 - lse2);
 }
 
+__device__ __forceinline__ u32x4 pack8(const f32x16& v, int base) {
+  return u32x4{pack_bf16(v[base + 0], v[base + 1]), pack_bf16(v[base + 2], v[base + 3]),
+               pack_bf16(v[base + 4], v[base + 5]), pack_bf16(v[base + 6], v[base + 7])};
+}
+
 // ---------------------------------------------------------------- dK, dV
 // Workgroup: 4 waves own keys [k0, k0 + 128), 32 per wave (one key column
 // per lane).  Per step: 64 query rows of one query head, Q and dO tiles in
 // LDS.  S = Q K^T and dP = dO V^T come out key-column-per-lane, so P and
 // dS are repacked in registers as the B operands of dV^T += dO^T P and
 // dK^T += Q^T dS, whose A operands are transposing LDS reads.
-template <int D, int MASK, int MOD>
+template <int D, int MASK, int MOD, bool BM>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BK = 128, BQ = 64, NQ = BQ / 32;
   constexpr int ROW = D * 2, TILE = BQ * ROW;
-  constexpr int KC = D / 16, DT = D / 32, NCH = D / 8, LOADS = BQ * NCH / 256;
-  static_assert(LOADS * 256 == BQ * NCH, "tile load must divide evenly");
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];  // [stage][Q, dO]
-  __shared__ __attribute__((aligned(16))) float slse[2][BQ];
-  __shared__ __attribute__((aligned(16))) float sdel[2][BQ];
-  __shared__ int sdoc[2][BQ];
+  constexpr int KC = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(16))) char sQ0[TILE], sO0[TILE], sQ1[TILE], sO1[TILE];
+  __shared__ __attribute__((aligned(16))) float sL0[BQ], sE0[BQ], sL1[BQ], sE1[BQ];
+  __shared__ __attribute__((aligned(16))) int sD0[BQ], sD1[BQ];
 
   int b, hk, kt;
   decode_work(blockIdx.x, a.B, a.Hkv, a.Hkv, a.n_kt, false, b, hk, kt);
@@ -101,19 +113,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   int doc_j = 0;
   if constexpr (MASK == MASK_DOCUMENT) doc_j = col_ok ? doc[kj] : -3;
 
-  // query steps per head
+  // query steps per head: analytic range or the block mask's q list of this key block
   constexpr int STEPS_PER_BLOCK = kMaskBlock / BQ;
-  const bool use_bm = a.bm.tile_state != nullptr;
   int qs_lo = 0, n_qs = 0;
   const int32_t* bm_list = nullptr;
   const uint8_t* bm_state = nullptr;
-  int bm_row = 0;
-  if (use_bm) {
+  if constexpr (BM) {
     const int bb = a.bm.n_b == 1 ? 0 : b;
     n_qs = a.bm.q_count[bb * a.bm.n_kv + kt] * STEPS_PER_BLOCK;
     bm_list = a.bm.q_index + (size_t)(bb * a.bm.n_kv + kt) * a.bm.n_q;
-    bm_state = a.bm.tile_state + (size_t)bb * a.bm.n_q * a.bm.n_kv;
-    bm_row = a.bm.n_kv;
+    bm_state = a.bm.tile_state + (size_t)bb * a.bm.n_q * a.bm.n_kv + kt;  // + qb * n_kv
   } else {
     int lo = 0, hi = Sq;
     if constexpr (MASK != MASK_NONE) lo = min(k0, Sq);
@@ -123,54 +132,30 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       n_qs = (hi + BQ - 1) / BQ - qs_lo;
     }
   }
-  auto step_q0 = [&](int s) -> int {
-    const int qs = s % n_qs;
-    if (use_bm) return bm_list[qs / STEPS_PER_BLOCK] * kMaskBlock + (qs % STEPS_PER_BLOCK) * BQ;
-    return (qs_lo + qs) * BQ;
-  };
   const int n_steps = G * n_qs;
-
-  u32x4 qr[LOADS], dr[LOADS];
-  float lr = 0.0f, er = 0.0f;
-  int docr = 0;
-  auto gload = [&](int s) {
-    const int hq = hk * G + s / n_qs, q0 = step_q0(s);
-    const uint16_t* Qh = (const uint16_t*)a.q + (size_t)(b * a.Hq + hq) * Sq * D;
-    const uint16_t* dOh = (const uint16_t*)a.dout + (size_t)(b * a.Hq + hq) * Sq * D;
-#pragma unroll
-    for (int p = 0; p < LOADS; ++p) {
-      const int id = tid + 256 * p, r = id / NCH, c = id % NCH, i = q0 + r;
-      if (i < Sq) {
-        qr[p] = *(const u32x4*)(Qh + (size_t)i * D + c * 8);
-        dr[p] = *(const u32x4*)(dOh + (size_t)i * D + c * 8);
-      } else {
-        qr[p] = u32x4{0, 0, 0, 0};
-        dr[p] = u32x4{0, 0, 0, 0};
-      }
-    }
-    if (tid < BQ) {
-      const int i = q0 + tid;
-      const size_t ri = (size_t)(b * a.Hq + hq) * Sq + i;
-      const float L = i < Sq ? a.lse[ri] : kNegInf;
-      // Rows past the end or with no admissible key contribute nothing.
-      lr = (L == kNegInf) ? __builtin_inff() : L * kLog2e;
-      er = i < Sq ? a.delta[ri] : 0.0f;
-      if constexpr (MASK == MASK_DOCUMENT) docr = i < Sq ? doc[i] : -4;
-    }
+  // Block index (block-mask path) or query-step index (analytic) of step s.
+  auto fetch_blk = [&](int s) -> int {
+    if (s >= n_steps) return 0;
+    if constexpr (BM) return bm_list[(s % n_qs) / STEPS_PER_BLOCK];
+    return qs_lo + s % n_qs;
   };
-  auto lstore = [&](int stage) {
-    char* qs = smem + stage * 2 * TILE;
-    char* ds = qs + TILE;
-#pragma unroll
-    for (int p = 0; p < LOADS; ++p) {
-      const int id = tid + 256 * p, r = id / NCH, c = id % NCH;
-      *(u32x4*)(qs + r * ROW + swz<D>(r, c) * 16) = qr[p];
-      *(u32x4*)(ds + r * ROW + swz<D>(r, c) * 16) = dr[p];
-    }
-    if (tid < BQ) {
-      slse[stage][tid] = lr;
-      sdel[stage][tid] = er;
-      if constexpr (MASK == MASK_DOCUMENT) sdoc[stage][tid] = docr;
+  auto query0 = [&](int s, int blk) -> int {
+    if constexpr (BM) return blk * kMaskBlock + ((s % n_qs) % STEPS_PER_BLOCK) * BQ;
+    return blk * BQ;
+  };
+
+  const __amdgpu_buffer_rsrc_t rsDoc = make_rsrc(doc, MASK == MASK_DOCUMENT ? (uint32_t)Skv * 4 : 0u);
+  auto issue = [&](int s, int blk, char* qn, char* on, float* ln, float* en, int* dn) {
+    const int hq = hk * G + s / n_qs, q0 = query0(s, blk);
+    const size_t head = (size_t)(b * a.Hq + hq) * Sq;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t*)a.q + head * D, (uint32_t)Sq * D * 2);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc((const uint16_t*)a.dout + head * D, (uint32_t)Sq * D * 2);
+    tile_to_lds<D, BQ>(rq, q0, qn, wave, lane);
+    tile_to_lds<D, BQ>(ro, q0, on, wave, lane);
+    if (wave == 0) ints_to_lds(make_rsrc(a.lse2 + head, (uint32_t)Sq * 4), q0, (int*)ln, lane);
+    if (wave == 1) ints_to_lds(make_rsrc(a.delta + head, (uint32_t)Sq * 4), q0, (int*)en, lane);
+    if constexpr (MASK == MASK_DOCUMENT) {
+      if (wave == 2) ints_to_lds(rsDoc, q0, dn, lane);
     }
   };
 
@@ -180,99 +165,94 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     dk[dt] = f32x16{};
     dv[dt] = f32x16{};
   }
-  if (n_steps > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
 
-  for (int s = 0; s < n_steps; ++s) {
-    const int cur = s & 1;
+  int blk_c = 0, blk_n = 0, st_c = 0, st_n = 0;
+  auto step = [&](int s, const char* qs, const char* ds, const float* ls, const float* es, const int* dcs,
+                  char* qn, char* on, float* ln, float* en, int* dn) {
     const bool have_next = s + 1 < n_steps;
-    if (have_next) gload(s + 1);
+    if (have_next) issue(s + 1, blk_n, qn, on, ln, en, dn);
+    const int blk_nn = fetch_blk(s + 2);
+    if constexpr (BM) st_n = have_next ? bm_state[(size_t)blk_n * a.bm.n_kv] : 0;
     const int hq = hk * G + s / n_qs;
-    const int q0 = step_q0(s);
+    const int q0 = query0(s, blk_c);
     int cls;
-    if (use_bm) {
-      const int qb = bm_list[(s % n_qs) / STEPS_PER_BLOCK];
-      cls = bm_state[qb * bm_row + kt] == TILE_FULL ? TILE_FULL : TILE_PARTIAL;
+    if constexpr (BM) {
+      cls = st_c == TILE_FULL ? TILE_FULL : TILE_PARTIAL;
     } else {
       cls = block_class<MASK>(q0, BQ, kw0, 32, Skv, window);
     }
+    if (q0 + BQ > Sq && cls == TILE_FULL) cls = TILE_PARTIAL;
     if (kw0 >= Skv || q0 >= Sq) cls = TILE_EMPTY;
 
     if (cls != TILE_EMPTY) {
-      const char* qs = smem + cur * 2 * TILE;
-      const char* ds = qs + TILE;
       const float slope = head_slope<MOD>(a.mod, hq, a.Hq);
-      f32x16 sp[NQ], dp[NQ];
+      const int ch = 2 * g16 + ((gi & 3) >> 1);
+      const int half = (gi & 1) * 8;
+      // One 32-row query subtile at a time keeps the live registers low.
 #pragma unroll
       for (int t = 0; t < NQ; ++t) {
-        sp[t] = f32x16{};
-        dp[t] = f32x16{};
+        f32x16 sp = f32x16{}, dp = f32x16{};
         const int r = 32 * t + l32;
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-          sp[t] = mfma_bf16(*(const u32x4*)(qs + r * ROW + swz<D>(r, 2 * c + hh) * 16), kf[c], sp[t]);
-          dp[t] = mfma_bf16(*(const u32x4*)(ds + r * ROW + swz<D>(r, 2 * c + hh) * 16), vf[c], dp[t]);
+          sp = mfma_bf16(*(const u32x4*)(qs + r * ROW + swz<D>(r, 2 * c + hh) * 16), kf[c], sp);
+          dp = mfma_bf16(*(const u32x4*)(ds + r * ROW + swz<D>(r, 2 * c + hh) * 16), vf[c], dp);
         }
-      }
-      // P and dS (register r of subtile t: query q0 + 32t + 8(r/4) + 4hh + r%4)
-#pragma unroll
-      for (int t = 0; t < NQ; ++t)
+        // P and dS (register r: query q0 + 32t + 8(r/4) + 4hh + r%4)
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
           const int ir = 32 * t + 8 * rq + 4 * hh;
-          const f32x4 L4 = *(const f32x4*)&slse[cur][ir];
-          const f32x4 E4 = *(const f32x4*)&sdel[cur][ir];
+          const f32x4 L4 = *(const f32x4*)&ls[ir];
+          const f32x4 E4 = *(const f32x4*)&es[ir];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = q0 + ir + e;
             float p, grad;
-            recompute_p<MOD>(sp[t][4 * rq + e], i, kj, slope, a, L4[e], p, grad);
+            recompute_p<MOD>(sp[4 * rq + e], i, kj, slope, a, L4[e], p, grad);
             if (cls == TILE_PARTIAL) {
               int di = 0;
-              if constexpr (MASK == MASK_DOCUMENT) di = sdoc[cur][ir + e];
-              const bool ok = col_ok && mask_ok<MASK>(i, kj, window, di, doc_j);
+              if constexpr (MASK == MASK_DOCUMENT) di = dcs[ir + e];
+              const bool ok = col_ok && i < Sq && mask_ok<MASK>(i, kj, window, di, doc_j);
               p = ok ? p : 0.0f;
             }
-            sp[t][4 * rq + e] = p;
-            dp[t][4 * rq + e] = p * (dp[t][4 * rq + e] - E4[e]) * grad;
+            sp[4 * rq + e] = p;
+            dp[4 * rq + e] = p * (dp[4 * rq + e] - E4[e]) * grad;
           }
         }
-      u32x4 pb[NQ][2], sb[NQ][2];
+        const u32x4 pb0 = pack8(sp, 0), pb1 = pack8(sp, 8);
+        const u32x4 sb0 = pack8(dp, 0), sb1 = pack8(dp, 8);
 #pragma unroll
-      for (int t = 0; t < NQ; ++t)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          pb[t][cc] = u32x4{pack_bf16(sp[t][8 * cc + 0], sp[t][8 * cc + 1]),
-                            pack_bf16(sp[t][8 * cc + 2], sp[t][8 * cc + 3]),
-                            pack_bf16(sp[t][8 * cc + 4], sp[t][8 * cc + 5]),
-                            pack_bf16(sp[t][8 * cc + 6], sp[t][8 * cc + 7])};
-          sb[t][cc] = u32x4{pack_bf16(dp[t][8 * cc + 0], dp[t][8 * cc + 1]),
-                            pack_bf16(dp[t][8 * cc + 2], dp[t][8 * cc + 3]),
-                            pack_bf16(dp[t][8 * cc + 4], dp[t][8 * cc + 5]),
-                            pack_bf16(dp[t][8 * cc + 6], dp[t][8 * cc + 7])};
-        }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int ch = 4 * dt + 2 * g16 + ((gi & 3) >> 1);
-        const int half = (gi & 1) * 8;
-#pragma unroll
-        for (int t = 0; t < NQ; ++t)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
           for (int cc = 0; cc < 2; ++cc) {
             const int r0 = 32 * t + 16 * cc + 4 * hh + (gi >> 2), r1 = r0 + 8;
-            const int o0 = r0 * ROW + swz<D>(r0, ch) * 16 + half, o1 = r1 * ROW + swz<D>(r1, ch) * 16 + half;
+            const int o0 = r0 * ROW + swz<D>(r0, 4 * dt + ch) * 16 + half;
+            const int o1 = r1 * ROW + swz<D>(r1, 4 * dt + ch) * 16 + half;
             const u32x2 dlo = lds_read_tr16(ds + o0), dhi = lds_read_tr16(ds + o1);
-            dv[dt] = mfma_bf16(u32x4{dlo[0], dlo[1], dhi[0], dhi[1]}, pb[t][cc], dv[dt]);
+            dv[dt] = mfma_bf16(u32x4{dlo[0], dlo[1], dhi[0], dhi[1]}, cc ? pb1 : pb0, dv[dt]);
             const u32x2 qlo = lds_read_tr16(qs + o0), qhi = lds_read_tr16(qs + o1);
-            dk[dt] = mfma_bf16(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, sb[t][cc], dk[dt]);
+            dk[dt] = mfma_bf16(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, cc ? sb1 : sb0, dk[dt]);
           }
       }
     }
-    if (have_next) lstore(cur ^ 1);
+    wait_loads();
     __syncthreads();
+    blk_c = blk_n;
+    st_c = st_n;
+    blk_n = blk_nn;
+  };
+
+  blk_c = fetch_blk(0);
+  blk_n = fetch_blk(1);
+  if constexpr (BM) st_c = n_steps > 0 ? bm_state[(size_t)blk_c * a.bm.n_kv] : 0;
+  if (n_steps > 0) {
+    issue(0, blk_c, sQ0, sO0, sL0, sE0, sD0);
+    wait_loads();
+  }
+  __syncthreads();
+  for (int s = 0; s < n_steps; s += 2) {
+    step(s, sQ0, sO0, sL0, sE0, sD0, sQ1, sO1, sL1, sE1, sD1);
+    if (s + 1 < n_steps) step(s + 1, sQ1, sO1, sL1, sE1, sD1, sQ0, sO0, sL0, sE0, sD0);
   }
 
   if (col_ok) {
@@ -296,13 +276,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 // column per lane, as in the forward kernel).  Per step: 64 keys, K and V
 // tiles in LDS.  S^T = K Q^T and dP^T = V dO^T give dS^T with a query per
 // lane; dQ^T += K^T dS^T takes K^T from transposing LDS reads.
-template <int D, int MASK, int MOD>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+template <int D, int MASK, int MOD, bool BM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdArgs a) {
   constexpr int BN = 64, NT = BN / 32;
   constexpr int ROW = D * 2, TILE = BN * ROW;
-  constexpr int KC = D / 16, DT = D / 32, NCH = D / 8, LOADS = BN * NCH / 256;
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];  // [stage][K, V]
-  __shared__ int sdoc[2][BN];
+  constexpr int KC = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(16))) char sK0[TILE], sV0[TILE], sK1[TILE], sV1[TILE];
+  __shared__ __attribute__((aligned(16))) int sD0[BN], sD1[BN];
 
   int b, hq, qt;
   decode_work(blockIdx.x, a.B, a.Hq, a.Hkv, a.n_qt, MASK == MASK_CAUSAL || MASK == MASK_DOCUMENT, b, hq,
@@ -323,12 +303,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     qf[c] = row_ok ? ((const u32x4*)Qrow)[2 * c + hh] : u32x4{0, 0, 0, 0};
     of[c] = row_ok ? ((const u32x4*)dOrow)[2 * c + hh] : u32x4{0, 0, 0, 0};
   }
-  float lse2 = __builtin_inff(), del = 0.0f;
-  if (row_ok) {
-    const float L = a.lse[ri];
-    lse2 = (L == kNegInf) ? __builtin_inff() : L * kLog2e;
-    del = a.delta[ri];
-  }
+  const float lse2 = row_ok ? a.lse2[ri] : __builtin_inff();
+  const float del = row_ok ? a.delta[ri] : 0.0f;
   const uint16_t* K = (const uint16_t*)a.k + (size_t)(b * a.Hkv + hk) * Skv * D;
   const uint16_t* V = (const uint16_t*)a.v + (size_t)(b * a.Hkv + hk) * Skv * D;
   const int32_t* doc = nullptr;
@@ -340,11 +316,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const float slope = head_slope<MOD>(a.mod, hq, a.Hq);
 
   constexpr int STEPS_PER_BLOCK = kMaskBlock / BN;
-  const bool use_bm = a.bm.tile_state != nullptr;
   int step_lo = 0, n_steps = 0;
   const int32_t* bm_list = nullptr;
   const uint8_t* bm_state = nullptr;
-  if (use_bm) {
+  if constexpr (BM) {
     const int bb = a.bm.n_b == 1 ? 0 : b;
     const int row = bb * a.bm.n_q + qt;
     n_steps = a.bm.kv_count[row] * STEPS_PER_BLOCK;
@@ -358,124 +333,103 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       n_steps = (hi + BN - 1) / BN - step_lo;
     }
   }
-  auto step_k0 = [&](int s) -> int {
-    if (use_bm) return bm_list[s / STEPS_PER_BLOCK] * kMaskBlock + (s % STEPS_PER_BLOCK) * BN;
-    return (step_lo + s) * BN;
+  auto fetch_blk = [&](int s) -> int {
+    if (s >= n_steps) return 0;
+    if constexpr (BM) return bm_list[s / STEPS_PER_BLOCK];
+    return step_lo + s;
+  };
+  auto key0 = [&](int s, int blk) -> int {
+    if constexpr (BM) return blk * kMaskBlock + (s % STEPS_PER_BLOCK) * BN;
+    return blk * BN;
   };
 
-  u32x4 kr[LOADS], vr[LOADS];
-  int docr = 0;
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int p = 0; p < LOADS; ++p) {
-      const int id = tid + 256 * p, r = id / NCH, c = id % NCH, j = k0 + r;
-      if (j < Skv) {
-        kr[p] = *(const u32x4*)(K + (size_t)j * D + c * 8);
-        vr[p] = *(const u32x4*)(V + (size_t)j * D + c * 8);
-      } else {
-        kr[p] = u32x4{0, 0, 0, 0};
-        vr[p] = u32x4{0, 0, 0, 0};
-      }
-    }
+  const __amdgpu_buffer_rsrc_t rsK = make_rsrc(K, (uint32_t)Skv * D * 2);
+  const __amdgpu_buffer_rsrc_t rsV = make_rsrc(V, (uint32_t)Skv * D * 2);
+  const __amdgpu_buffer_rsrc_t rsD = make_rsrc(doc, MASK == MASK_DOCUMENT ? (uint32_t)Skv * 4 : 0u);
+  auto issue = [&](int k0, char* kn, char* vn, int* dn) {
+    tile_to_lds<D, BN>(rsK, k0, kn, wave, lane);
+    tile_to_lds<D, BN>(rsV, k0, vn, wave, lane);
     if constexpr (MASK == MASK_DOCUMENT) {
-      if (tid < BN) docr = (k0 + tid < Skv) ? doc[k0 + tid] : -2;
-    }
-  };
-  auto lstore = [&](int stage) {
-    char* ks = smem + stage * 2 * TILE;
-    char* vs = ks + TILE;
-#pragma unroll
-    for (int p = 0; p < LOADS; ++p) {
-      const int id = tid + 256 * p, r = id / NCH, c = id % NCH;
-      *(u32x4*)(ks + r * ROW + swz<D>(r, c) * 16) = kr[p];
-      *(u32x4*)(vs + r * ROW + swz<D>(r, c) * 16) = vr[p];
-    }
-    if constexpr (MASK == MASK_DOCUMENT) {
-      if (tid < BN) sdoc[stage][tid] = docr;
+      if (wave == 0) ints_to_lds(rsD, k0, dn, lane);
     }
   };
 
   f32x16 dq[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x16{};
-  if (n_steps > 0) {
-    gload(step_k0(0));
-    lstore(0);
-  }
-  __syncthreads();
 
-  for (int s = 0; s < n_steps; ++s) {
-    const int cur = s & 1;
-    const int k0 = step_k0(s);
+  int blk_c = 0, blk_n = 0, st_c = 0, st_n = 0;
+  auto step = [&](int s, const char* ks, const char* vs, const int* dcs, char* kn, char* vn, int* dn) {
+    const int k0 = key0(s, blk_c);
     const bool have_next = s + 1 < n_steps;
-    if (have_next) gload(step_k0(s + 1));
+    if (have_next) issue(key0(s + 1, blk_n), kn, vn, dn);
+    const int blk_nn = fetch_blk(s + 2);
+    if constexpr (BM) st_n = have_next ? bm_state[blk_n] : 0;
     int cls;
-    if (use_bm) {
-      cls = (k0 >= Skv) ? TILE_EMPTY
-                        : (bm_state[bm_list[s / STEPS_PER_BLOCK]] == TILE_FULL ? TILE_FULL : TILE_PARTIAL);
+    if constexpr (BM) {
+      cls = (k0 >= Skv) ? TILE_EMPTY : (st_c == TILE_FULL ? TILE_FULL : TILE_PARTIAL);
     } else {
       cls = block_class<MASK>(qw0, 32, k0, BN, Skv, window);
     }
     if (qw0 >= Sq) cls = TILE_EMPTY;
 
     if (cls != TILE_EMPTY) {
-      const char* ks = smem + cur * 2 * TILE;
-      const char* vs = ks + TILE;
-      f32x16 st[NT], dpt[NT];
+      const int ch = 2 * g16 + ((gi & 3) >> 1);
+      const int half = (gi & 1) * 8;
+      // One 32-key subtile at a time keeps the live registers low.
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        st[t] = f32x16{};
-        dpt[t] = f32x16{};
+        f32x16 st = f32x16{}, dpt = f32x16{};
         const int r = 32 * t + l32;
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-          st[t] = mfma_bf16(*(const u32x4*)(ks + r * ROW + swz<D>(r, 2 * c + hh) * 16), qf[c], st[t]);
-          dpt[t] = mfma_bf16(*(const u32x4*)(vs + r * ROW + swz<D>(r, 2 * c + hh) * 16), of[c], dpt[t]);
+          st = mfma_bf16(*(const u32x4*)(ks + r * ROW + swz<D>(r, 2 * c + hh) * 16), qf[c], st);
+          dpt = mfma_bf16(*(const u32x4*)(vs + r * ROW + swz<D>(r, 2 * c + hh) * 16), of[c], dpt);
         }
-      }
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int jr = 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+        for (int rr = 0; rr < 16; ++rr) {
+          const int jr = 32 * t + 8 * (rr >> 2) + 4 * hh + (rr & 3);
           const int j = k0 + jr;
           float p, grad;
-          BwdArgs const& aa = a;
-          recompute_p<MOD>(st[t][r], qi, j, slope, aa, lse2, p, grad);
+          recompute_p<MOD>(st[rr], qi, j, slope, a, lse2, p, grad);
           if (cls == TILE_PARTIAL) {
             int dj = 0;
-            if constexpr (MASK == MASK_DOCUMENT) dj = sdoc[cur][jr];
+            if constexpr (MASK == MASK_DOCUMENT) dj = dcs[jr];
             const bool ok = j < Skv && mask_ok<MASK>(qi, j, window, doc_i, dj);
             p = ok ? p : 0.0f;
           }
-          dpt[t][r] = p * (dpt[t][r] - del) * grad;
+          dpt[rr] = p * (dpt[rr] - del) * grad;
         }
-      u32x4 sb[NT][2];
+        const u32x4 sb0 = pack8(dpt, 0), sb1 = pack8(dpt, 8);
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-          sb[t][cc] = u32x4{pack_bf16(dpt[t][8 * cc + 0], dpt[t][8 * cc + 1]),
-                            pack_bf16(dpt[t][8 * cc + 2], dpt[t][8 * cc + 3]),
-                            pack_bf16(dpt[t][8 * cc + 4], dpt[t][8 * cc + 5]),
-                            pack_bf16(dpt[t][8 * cc + 6], dpt[t][8 * cc + 7])};
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int ch = 4 * dt + 2 * g16 + ((gi & 3) >> 1);
-        const int half = (gi & 1) * 8;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
           for (int cc = 0; cc < 2; ++cc) {
             const int r0 = 32 * t + 16 * cc + 4 * hh + (gi >> 2), r1 = r0 + 8;
-            const u32x2 lo = lds_read_tr16(ks + r0 * ROW + swz<D>(r0, ch) * 16 + half);
-            const u32x2 hi = lds_read_tr16(ks + r1 * ROW + swz<D>(r1, ch) * 16 + half);
-            dq[dt] = mfma_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, sb[t][cc], dq[dt]);
+            const u32x2 lo = lds_read_tr16(ks + r0 * ROW + swz<D>(r0, 4 * dt + ch) * 16 + half);
+            const u32x2 hi = lds_read_tr16(ks + r1 * ROW + swz<D>(r1, 4 * dt + ch) * 16 + half);
+            dq[dt] = mfma_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, cc ? sb1 : sb0, dq[dt]);
           }
       }
     }
-    if (have_next) lstore(cur ^ 1);
+    wait_loads();
     __syncthreads();
+    blk_c = blk_n;
+    st_c = st_n;
+    blk_n = blk_nn;
+  };
+
+  blk_c = fetch_blk(0);
+  blk_n = fetch_blk(1);
+  if constexpr (BM) st_c = n_steps > 0 ? bm_state[blk_c] : 0;
+  if (n_steps > 0) {
+    issue(key0(0, blk_c), sK0, sV0, sD0);
+    wait_loads();
+  }
+  __syncthreads();
+  for (int s = 0; s < n_steps; s += 2) {
+    step(s, sK0, sV0, sD0, sK1, sV1, sD1);
+    if (s + 1 < n_steps) step(s + 1, sK1, sV1, sD1, sK0, sV0, sD0);
   }
 
   if (row_ok) {
@@ -491,38 +445,45 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-template <int D, int MASK, int MOD>
+template <int D, int MASK, int MOD, bool BM>
 static hipError_t launch_bwd_mm(const BwdArgs& a, int phases, hipStream_t st) {
   const long rows = (long)a.B * a.Hq * a.Sq;
   const int rows_per_block = 256 / (D / 8);
   if ((phases & 1) && rows > 0) {
     hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
-                       dim3(256), 0, st, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows);
+                       dim3(256), 0, st, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, a.delta,
+                       const_cast<float*>(a.lse2), rows);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   // dK, dV are written for every key (zero when no query sees it).
   if ((phases & 2) && (long)a.B * a.Hkv * a.n_kt > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK, MOD>), dim3((unsigned)(a.B * a.Hkv * a.n_kt)), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK, MOD, BM>), dim3((unsigned)(a.B * a.Hkv * a.n_kt)), dim3(256), 0,
                        st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if ((phases & 4) && rows > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, MASK, MOD>), dim3((unsigned)(a.B * a.Hq * a.n_qt)), dim3(256), 0, st,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, MASK, MOD, BM>), dim3((unsigned)(a.B * a.Hq * a.n_qt)), dim3(256), 0, st,
                        a);
     return hipGetLastError();
   }
   return hipSuccess;
 }
 
+template <int D, int MASK, int MOD>
+static hipError_t launch_bwd_bm(const BwdArgs& a, int phases, hipStream_t st) {
+  return a.bm.tile_state != nullptr ? launch_bwd_mm<D, MASK, MOD, true>(a, phases, st)
+                                    : launch_bwd_mm<D, MASK, MOD, false>(a, phases, st);
+}
+
 template <int D, int MASK>
 static hipError_t launch_bwd_mask(const BwdArgs& a, int mod, int phases, hipStream_t st) {
   switch (mod) {
-    case MOD_NONE: return launch_bwd_mm<D, MASK, MOD_NONE>(a, phases, st);
-    case MOD_ALIBI: return launch_bwd_mm<D, MASK, MOD_ALIBI>(a, phases, st);
-    case MOD_SOFTCAP: return launch_bwd_mm<D, MASK, MOD_SOFTCAP>(a, phases, st);
-    default: return launch_bwd_mm<D, MASK, MOD_BOOST>(a, phases, st);
+    case MOD_NONE: return launch_bwd_bm<D, MASK, MOD_NONE>(a, phases, st);
+    case MOD_ALIBI: return launch_bwd_bm<D, MASK, MOD_ALIBI>(a, phases, st);
+    case MOD_SOFTCAP: return launch_bwd_bm<D, MASK, MOD_SOFTCAP>(a, phases, st);
+    default: return launch_bwd_bm<D, MASK, MOD_BOOST>(a, phases, st);
   }
 }
 
