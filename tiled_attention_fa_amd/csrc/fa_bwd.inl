@@ -76,18 +76,22 @@ __device__ __forceinline__ u32x4 pack8(const f32x16& v, int base) {
 
 // ---------------------------------------------------------------- dK, dV
 // Workgroup: 4 waves own keys [k0, k0 + 128), 32 per wave (one key column
-// per lane).  Per step: 64 query rows of one query head, Q and dO tiles in
-// LDS.  S = Q K^T and dP = dO V^T come out key-column-per-lane, so P and
-// dS are repacked in registers as the B operands of dV^T += dO^T P and
-// dK^T += Q^T dS, whose A operands are transposing LDS reads.
+// per lane).  K rows stay in registers; the workgroup's 128 V rows sit in
+// LDS for the whole kernel.  Per step: 32 query rows of one query head, Q
+// and dO tiles in LDS.  S = Q K^T and dP = dO V^T come out key-column-per-
+// lane, so P and dS are repacked in registers as the B operands of
+// dV^T += dO^T P and dK^T += Q^T dS, whose A operands are transposing LDS
+// reads.  Two workgroups fit per CU (2 waves per SIMD).
 template <int D, int MASK, int MOD, bool BM>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int BK = 128, BQ = 64, NQ = BQ / 32;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int BK = 128, BQ = 32;
   constexpr int ROW = D * 2, TILE = BQ * ROW;
   constexpr int KC = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(16))) char sV[BK * ROW];
   __shared__ __attribute__((aligned(16))) char sQ0[TILE], sO0[TILE], sQ1[TILE], sO1[TILE];
-  __shared__ __attribute__((aligned(16))) float sL0[BQ], sE0[BQ], sL1[BQ], sE1[BQ];
-  __shared__ __attribute__((aligned(16))) int sD0[BQ], sD1[BQ];
+  // 64 entries each: one per lane of the loading wave (the last 32 are unused).
+  __shared__ __attribute__((aligned(16))) float sL0[64], sE0[64], sL1[64], sE1[64];
+  __shared__ __attribute__((aligned(16))) int sD0[64], sD1[64];
 
   int b, hk, kt;
   decode_work(blockIdx.x, a.B, a.Hkv, a.Hkv, a.n_kt, false, b, hk, kt);
@@ -96,18 +100,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   const int Sq = a.Sq, Skv = a.Skv, G = a.G, window = a.mask.window;
   const int k0 = kt * BK, kw0 = k0 + 32 * wave, kj = kw0 + l32;
   const bool col_ok = kj < Skv;
+  const int vrow = 32 * wave + l32;  // this lane's key row in sV
 
   const uint16_t* Kh = (const uint16_t*)a.k + (size_t)(b * a.Hkv + hk) * Skv * D;
   const uint16_t* Vh = (const uint16_t*)a.v + (size_t)(b * a.Hkv + hk) * Skv * D;
-  u32x4 kf[KC], vf[KC];
+  u32x4 kf[KC];
   {
     const u32x4* ks = (const u32x4*)(Kh + (size_t)(col_ok ? kj : 0) * D);
-    const u32x4* vs = (const u32x4*)(Vh + (size_t)(col_ok ? kj : 0) * D);
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      kf[c] = col_ok ? ks[2 * c + hh] : u32x4{0, 0, 0, 0};
-      vf[c] = col_ok ? vs[2 * c + hh] : u32x4{0, 0, 0, 0};
-    }
+    for (int c = 0; c < KC; ++c) kf[c] = col_ok ? ks[2 * c + hh] : u32x4{0, 0, 0, 0};
   }
   const int32_t* doc = (MASK == MASK_DOCUMENT) ? a.mask.doc_ids + (size_t)b * Skv : nullptr;
   int doc_j = 0;
@@ -188,52 +189,48 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       const float slope = head_slope<MOD>(a.mod, hq, a.Hq);
       const int ch = 2 * g16 + ((gi & 3) >> 1);
       const int half = (gi & 1) * 8;
-      // One 32-row query subtile at a time keeps the live registers low.
+      f32x16 sp = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int t = 0; t < NQ; ++t) {
-        f32x16 sp = f32x16{}, dp = f32x16{};
-        const int r = 32 * t + l32;
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-          sp = mfma_bf16(*(const u32x4*)(qs + r * ROW + swz<D>(r, 2 * c + hh) * 16), kf[c], sp);
-          dp = mfma_bf16(*(const u32x4*)(ds + r * ROW + swz<D>(r, 2 * c + hh) * 16), vf[c], dp);
-        }
-        // P and dS (register r: query q0 + 32t + 8(r/4) + 4hh + r%4)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int ir = 32 * t + 8 * rq + 4 * hh;
-          const f32x4 L4 = *(const f32x4*)&ls[ir];
-          const f32x4 E4 = *(const f32x4*)&es[ir];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = q0 + ir + e;
-            float p, grad;
-            recompute_p<MOD>(sp[4 * rq + e], i, kj, slope, a, L4[e], p, grad);
-            if (cls == TILE_PARTIAL) {
-              int di = 0;
-              if constexpr (MASK == MASK_DOCUMENT) di = dcs[ir + e];
-              const bool ok = col_ok && i < Sq && mask_ok<MASK>(i, kj, window, di, doc_j);
-              p = ok ? p : 0.0f;
-            }
-            sp[4 * rq + e] = p;
-            dp[4 * rq + e] = p * (dp[4 * rq + e] - E4[e]) * grad;
-          }
-        }
-        const u32x4 pb0 = pack8(sp, 0), pb1 = pack8(sp, 8);
-        const u32x4 sb0 = pack8(dp, 0), sb1 = pack8(dp, 8);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int cc = 0; cc < 2; ++cc) {
-            const int r0 = 32 * t + 16 * cc + 4 * hh + (gi >> 2), r1 = r0 + 8;
-            const int o0 = r0 * ROW + swz<D>(r0, 4 * dt + ch) * 16 + half;
-            const int o1 = r1 * ROW + swz<D>(r1, 4 * dt + ch) * 16 + half;
-            const u32x2 dlo = lds_read_tr16(ds + o0), dhi = lds_read_tr16(ds + o1);
-            dv[dt] = mfma_bf16(u32x4{dlo[0], dlo[1], dhi[0], dhi[1]}, cc ? pb1 : pb0, dv[dt]);
-            const u32x2 qlo = lds_read_tr16(qs + o0), qhi = lds_read_tr16(qs + o1);
-            dk[dt] = mfma_bf16(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, cc ? sb1 : sb0, dk[dt]);
-          }
+      for (int c = 0; c < KC; ++c) {
+        sp = mfma_bf16(*(const u32x4*)(qs + l32 * ROW + swz<D>(l32, 2 * c + hh) * 16), kf[c], sp);
+        dp = mfma_bf16(*(const u32x4*)(ds + l32 * ROW + swz<D>(l32, 2 * c + hh) * 16),
+                       *(const u32x4*)(sV + vrow * ROW + swz<D>(vrow, 2 * c + hh) * 16), dp);
       }
+      // P and dS (register r: query q0 + 8(r/4) + 4hh + r%4)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int ir = 8 * rq + 4 * hh;
+        const f32x4 L4 = *(const f32x4*)&ls[ir];
+        const f32x4 E4 = *(const f32x4*)&es[ir];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = q0 + ir + e;
+          float p, grad;
+          recompute_p<MOD>(sp[4 * rq + e], i, kj, slope, a, L4[e], p, grad);
+          if (cls == TILE_PARTIAL) {
+            int di = 0;
+            if constexpr (MASK == MASK_DOCUMENT) di = dcs[ir + e];
+            const bool ok = col_ok && i < Sq && mask_ok<MASK>(i, kj, window, di, doc_j);
+            p = ok ? p : 0.0f;
+          }
+          sp[4 * rq + e] = p;
+          dp[4 * rq + e] = p * (dp[4 * rq + e] - E4[e]) * grad;
+        }
+      }
+      const u32x4 pb0 = pack8(sp, 0), pb1 = pack8(sp, 8);
+      const u32x4 sb0 = pack8(dp, 0), sb1 = pack8(dp, 8);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const int r0 = 16 * cc + 4 * hh + (gi >> 2), r1 = r0 + 8;
+          const int o0 = r0 * ROW + swz<D>(r0, 4 * dt + ch) * 16 + half;
+          const int o1 = r1 * ROW + swz<D>(r1, 4 * dt + ch) * 16 + half;
+          const u32x2 dlo = lds_read_tr16(ds + o0), dhi = lds_read_tr16(ds + o1);
+          dv[dt] = mfma_bf16(u32x4{dlo[0], dlo[1], dhi[0], dhi[1]}, cc ? pb1 : pb0, dv[dt]);
+          const u32x2 qlo = lds_read_tr16(qs + o0), qhi = lds_read_tr16(qs + o1);
+          dk[dt] = mfma_bf16(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, cc ? sb1 : sb0, dk[dt]);
+        }
     }
     wait_loads();
     __syncthreads();
@@ -246,6 +243,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   blk_n = fetch_blk(1);
   if constexpr (BM) st_c = n_steps > 0 ? bm_state[(size_t)blk_c * a.bm.n_kv] : 0;
   if (n_steps > 0) {
+    tile_to_lds<D, BK>(make_rsrc(Vh, (uint32_t)Skv * D * 2), k0, sV, wave, lane);
     issue(0, blk_c, sQ0, sO0, sL0, sE0, sD0);
     wait_loads();
   }
