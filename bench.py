@@ -104,6 +104,9 @@ def main():
     ap.add_argument("--workload", default="causal_fwd_bwd")
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads of the oracle CPU baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (3 times) and exit: the reference for "
+                         "scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -116,6 +119,15 @@ def main():
     import tiled_attention_fa_amd as fa
     from tiled_attention_fa_amd import flops
 
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
     fa.lib()
     if args.workload not in synth.WORKLOADS:
         sys.exit(f"unknown workload {args.workload}; choose from {sorted(synth.WORKLOADS)}")
