@@ -202,19 +202,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (cls != TILE_EMPTY) {
       // ---- S^T = K Q^T  (lane: query column qi; register r: key 8(r/4) + 4hh + r%4)
       f32x16 st[NT];
+      if constexpr (F32) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        st[t] = f32x16{};
-        const int r = 32 * t + l32;
-        const char* krow = ks + r * ROW;
-        if constexpr (F32) {
+        for (int t = 0; t < NT; ++t) {
+          st[t] = f32x16{};
+          const char* krow = ks + (32 * t + l32) * ROW;
 #pragma unroll
           for (int c = 0; c < KC; ++c) st[t] = mfma_f32(((const float*)krow)[2 * c + hh], qs[c], st[t]);
-        } else {
-#pragma unroll
-          for (int c = 0; c < KC; ++c)
-            st[t] = mfma_bf16(*(const u32x4*)(krow + swz<D>(r, 2 * c + hh) * 16), qf[c], st[t]);
         }
+      } else {
+        // The NT accumulation chains alternate; LDS reads run 4 ahead of the MFMAs.
+#pragma unroll
+        for (int t = 0; t < NT; ++t) st[t] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const int r = 32 * t + l32;
+            st[t] = mfma_bf16(*(const u32x4*)(ks + r * ROW + swz<D>(r, 2 * c + hh) * 16), qf[c], st[t]);
+          }
+        constexpr int NM = KC * NT;
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < NM - 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
       // ---- scores to log2 units, modifier, mask; block max
       float mb = kNegInf;
@@ -308,6 +322,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
               acc[dt] = mfma_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[t][cc], acc[dt]);
             }
         }
+        // Transposing reads run two MFMAs (4 reads) ahead.
+        constexpr int NM = DT * NT * 2;
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+        for (int i = 0; i < NM - 2; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
       }
     }
 
