@@ -61,8 +61,22 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    _check_no_missing_kernels(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def _check_no_missing_kernels(path: str) -> None:
+    """A kernel whose host-side launch stub was not emitted leaves an undefined
+    symbol of the library's own namespace that only fails at load time; fail
+    the build instead."""
+    nm = shutil.which("nm") or "/usr/bin/nm"
+    r = subprocess.run([nm, "-D", "--undefined-only", path], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"nm failed on {path}:\n{r.stderr}")
+    missing = [ln.split()[-1] for ln in r.stdout.splitlines() if "_ZN6miattn" in ln]
+    if missing:
+        raise RuntimeError(f"{len(missing)} undefined library symbols, e.g. {missing[:3]}")
 
 
 if __name__ == "__main__":

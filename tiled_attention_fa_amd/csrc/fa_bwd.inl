@@ -14,6 +14,8 @@
 // forward pass).  Nothing is accumulated with atomics, so the results are
 // deterministic.  Q/dO (resp. K/V) tiles go straight from memory into
 // per-stage LDS objects, with the step loop unrolled by two.
+#include <type_traits>
+
 #include "fa_device.h"
 
 namespace miattn {
@@ -95,7 +97,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   int b, hk, kt;
   decode_work(blockIdx.x, a.B, a.Hkv, a.Hkv, a.n_kt, false, b, hk, kt);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = wave_uniform(tid >> 6);  // uniform: per-wave branches stay scalar
   const int gi = lane & 15, g16 = (lane >> 4) & 1;
   const int Sq = a.Sq, Skv = a.Skv, G = a.G, window = a.mask.window;
   const int k0 = kt * BK, kw0 = k0 + 32 * wave, kj = kw0 + l32;
@@ -134,29 +137,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
   const int n_steps = G * n_qs;
-  // Block index (block-mask path) or query-step index (analytic) of step s.
-  auto fetch_blk = [&](int s) -> int {
-    if (s >= n_steps) return 0;
-    if constexpr (BM) return bm_list[(s % n_qs) / STEPS_PER_BLOCK];
-    return qs_lo + s % n_qs;
+  // Position of a step: query head g of the GQA group, query step j of that
+  // head.  Steps run g-major; positions advance by counting, not dividing.
+  struct Pos {
+    int g, j;
   };
-  auto query0 = [&](int s, int blk) -> int {
-    if constexpr (BM) return blk * kMaskBlock + ((s % n_qs) % STEPS_PER_BLOCK) * BQ;
+  auto advance = [&](Pos p) -> Pos {
+    if (++p.j == n_qs) {
+      p.j = 0;
+      ++p.g;
+    }
+    return p;
+  };
+  // Block index (block-mask path) or query-step index (analytic) of step s.
+  auto fetch_blk = [&](int s, Pos p) -> int {
+    if (s >= n_steps) return 0;
+    if constexpr (BM) return bm_list[p.j / STEPS_PER_BLOCK];
+    return qs_lo + p.j;
+  };
+  auto query0 = [&](Pos p, int blk) -> int {
+    if constexpr (BM) return blk * kMaskBlock + (p.j % STEPS_PER_BLOCK) * BQ;
     return blk * BQ;
   };
 
-  const __amdgpu_buffer_rsrc_t rsDoc = make_rsrc(doc, MASK == MASK_DOCUMENT ? (uint32_t)Skv * 4 : 0u);
-  auto issue = [&](int s, int blk, char* qn, char* on, float* ln, float* en, int* dn) {
-    const int hq = hk * G + s / n_qs, q0 = query0(s, blk);
+  auto issue = [&](Pos p, int blk, char* qn, char* on, float* ln, float* en, int* dn) {
+    const int hq = hk * G + p.g, q0 = query0(p, blk);
     const size_t head = (size_t)(b * a.Hq + hq) * Sq;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const uint16_t*)a.q + head * D, (uint32_t)Sq * D * 2);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc((const uint16_t*)a.dout + head * D, (uint32_t)Sq * D * 2);
-    tile_to_lds<D, BQ>(rq, q0, qn, wave, lane);
-    tile_to_lds<D, BQ>(ro, q0, on, wave, lane);
-    if (wave == 0) ints_to_lds(make_rsrc(a.lse2 + head, (uint32_t)Sq * 4), q0, (int*)ln, lane);
-    if (wave == 1) ints_to_lds(make_rsrc(a.delta + head, (uint32_t)Sq * 4), q0, (int*)en, lane);
+    tile_load<D, BQ>(rows_rsrc((const uint16_t*)a.q + head * D, Sq, q0, ROW), qn, wave, lane);
+    tile_load<D, BQ>(rows_rsrc((const uint16_t*)a.dout + head * D, Sq, q0, ROW), on, wave, lane);
+    if (wave == 0) ints_to_lds(a.lse2 + head, Sq, q0, (int*)ln, lane);
+    if (wave == 1) ints_to_lds(a.delta + head, Sq, q0, (int*)en, lane);
     if constexpr (MASK == MASK_DOCUMENT) {
-      if (wave == 2) ints_to_lds(rsDoc, q0, dn, lane);
+      if (wave == 2) ints_to_lds(doc, Skv, q0, dn, lane);
     }
   };
 
@@ -168,14 +180,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   int blk_c = 0, blk_n = 0, st_c = 0, st_n = 0;
+  Pos pc{0, 0};
+  Pos pn = advance(pc);
+  Pos pnn = advance(pn);
   auto step = [&](int s, const char* qs, const char* ds, const float* ls, const float* es, const int* dcs,
                   char* qn, char* on, float* ln, float* en, int* dn) {
     const bool have_next = s + 1 < n_steps;
-    if (have_next) issue(s + 1, blk_n, qn, on, ln, en, dn);
-    const int blk_nn = fetch_blk(s + 2);
+    if (have_next) issue(pn, blk_n, qn, on, ln, en, dn);
+    const int blk_nn = fetch_blk(s + 2, pnn);
     if constexpr (BM) st_n = have_next ? bm_state[(size_t)blk_n * a.bm.n_kv] : 0;
-    const int hq = hk * G + s / n_qs;
-    const int q0 = query0(s, blk_c);
+    const int hq = hk * G + pc.g;
+    const int q0 = query0(pc, blk_c);
     int cls;
     if constexpr (BM) {
       cls = st_c == TILE_FULL ? TILE_FULL : TILE_PARTIAL;
@@ -196,26 +211,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         dp = mfma_bf16(*(const u32x4*)(ds + l32 * ROW + swz<D>(l32, 2 * c + hh) * 16),
                        *(const u32x4*)(sV + vrow * ROW + swz<D>(vrow, 2 * c + hh) * 16), dp);
       }
-      // P and dS (register r: query q0 + 8(r/4) + 4hh + r%4)
+      // P and dS (register r: query q0 + 8(r/4) + 4hh + r%4).  Full tiles
+      // take a branch without the mask test.
+      auto pds = [&](auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int ir = 8 * rq + 4 * hh;
-        const f32x4 L4 = *(const f32x4*)&ls[ir];
-        const f32x4 E4 = *(const f32x4*)&es[ir];
+        for (int rq = 0; rq < 4; ++rq) {
+          const int ir = 8 * rq + 4 * hh;
+          const f32x4 L4 = *(const f32x4*)&ls[ir];
+          const f32x4 E4 = *(const f32x4*)&es[ir];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = q0 + ir + e;
-          float p, grad;
-          recompute_p<MOD>(sp[4 * rq + e], i, kj, slope, a, L4[e], p, grad);
-          if (cls == TILE_PARTIAL) {
-            int di = 0;
-            if constexpr (MASK == MASK_DOCUMENT) di = dcs[ir + e];
-            const bool ok = col_ok && i < Sq && mask_ok<MASK>(i, kj, window, di, doc_j);
-            p = ok ? p : 0.0f;
+          for (int e = 0; e < 4; ++e) {
+            const int i = q0 + ir + e;
+            float p, grad;
+            recompute_p<MOD>(sp[4 * rq + e], i, kj, slope, a, L4[e], p, grad);
+            if constexpr (MASKED) {
+              int di = 0;
+              if constexpr (MASK == MASK_DOCUMENT) di = dcs[ir + e];
+              const bool ok = col_ok && i < Sq && mask_ok<MASK>(i, kj, window, di, doc_j);
+              p = ok ? p : 0.0f;
+            }
+            sp[4 * rq + e] = p;
+            dp[4 * rq + e] = p * (dp[4 * rq + e] - E4[e]) * grad;
           }
-          sp[4 * rq + e] = p;
-          dp[4 * rq + e] = p * (dp[4 * rq + e] - E4[e]) * grad;
         }
+      };
+      if (cls == TILE_PARTIAL) {
+        pds(std::true_type{});
+      } else {
+        pds(std::false_type{});
       }
       const u32x4 pb0 = pack8(sp, 0), pb1 = pack8(sp, 8);
       const u32x4 sb0 = pack8(dp, 0), sb1 = pack8(dp, 8);
@@ -237,14 +261,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     blk_c = blk_n;
     st_c = st_n;
     blk_n = blk_nn;
+    pc = pn;
+    pn = pnn;
+    pnn = advance(pnn);
   };
 
-  blk_c = fetch_blk(0);
-  blk_n = fetch_blk(1);
+  blk_c = fetch_blk(0, pc);
+  blk_n = fetch_blk(1, pn);
   if constexpr (BM) st_c = n_steps > 0 ? bm_state[(size_t)blk_c * a.bm.n_kv] : 0;
   if (n_steps > 0) {
-    tile_to_lds<D, BK>(make_rsrc(Vh, (uint32_t)Skv * D * 2), k0, sV, wave, lane);
-    issue(0, blk_c, sQ0, sO0, sL0, sE0, sD0);
+    tile_load<D, BK>(rows_rsrc(Vh, Skv, k0, ROW), sV, wave, lane);
+    issue(pc, blk_c, sQ0, sO0, sL0, sE0, sD0);
     wait_loads();
   }
   __syncthreads();
@@ -286,7 +313,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   decode_work(blockIdx.x, a.B, a.Hq, a.Hkv, a.n_qt, MASK == MASK_CAUSAL || MASK == MASK_DOCUMENT, b, hq,
               qt);
   const int hk = hq / a.G;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = wave_uniform(tid >> 6);  // uniform: per-wave branches stay scalar
   const int gi = lane & 15, g16 = (lane >> 4) & 1;
   const int Sq = a.Sq, Skv = a.Skv, window = a.mask.window;
   const int q0 = qt * kTileQ, qw0 = q0 + 32 * wave, qi = qw0 + l32;
@@ -341,14 +369,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return blk * BN;
   };
 
-  const __amdgpu_buffer_rsrc_t rsK = make_rsrc(K, (uint32_t)Skv * D * 2);
-  const __amdgpu_buffer_rsrc_t rsV = make_rsrc(V, (uint32_t)Skv * D * 2);
-  const __amdgpu_buffer_rsrc_t rsD = make_rsrc(doc, MASK == MASK_DOCUMENT ? (uint32_t)Skv * 4 : 0u);
   auto issue = [&](int k0, char* kn, char* vn, int* dn) {
-    tile_to_lds<D, BN>(rsK, k0, kn, wave, lane);
-    tile_to_lds<D, BN>(rsV, k0, vn, wave, lane);
+    tile_load<D, BN>(rows_rsrc(K, Skv, k0, ROW), kn, wave, lane);
+    tile_load<D, BN>(rows_rsrc(V, Skv, k0, ROW), vn, wave, lane);
     if constexpr (MASK == MASK_DOCUMENT) {
-      if (wave == 0) ints_to_lds(rsD, k0, dn, lane);
+      if (wave == 0) ints_to_lds(doc, Skv, k0, dn, lane);
     }
   };
 
@@ -384,19 +409,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           st = mfma_bf16(*(const u32x4*)(ks + r * ROW + swz<D>(r, 2 * c + hh) * 16), qf[c], st);
           dpt = mfma_bf16(*(const u32x4*)(vs + r * ROW + swz<D>(r, 2 * c + hh) * 16), of[c], dpt);
         }
+        // Full tiles take a branch without the mask test.
+        auto pds = [&](auto masked) {
+          constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int jr = 32 * t + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-          const int j = k0 + jr;
-          float p, grad;
-          recompute_p<MOD>(st[rr], qi, j, slope, a, lse2, p, grad);
-          if (cls == TILE_PARTIAL) {
-            int dj = 0;
-            if constexpr (MASK == MASK_DOCUMENT) dj = dcs[jr];
-            const bool ok = j < Skv && mask_ok<MASK>(qi, j, window, doc_i, dj);
-            p = ok ? p : 0.0f;
+          for (int rr = 0; rr < 16; ++rr) {
+            const int jr = 32 * t + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+            const int j = k0 + jr;
+            float p, grad;
+            recompute_p<MOD>(st[rr], qi, j, slope, a, lse2, p, grad);
+            if constexpr (MASKED) {
+              int dj = 0;
+              if constexpr (MASK == MASK_DOCUMENT) dj = dcs[jr];
+              const bool ok = j < Skv && mask_ok<MASK>(qi, j, window, doc_i, dj);
+              p = ok ? p : 0.0f;
+            }
+            dpt[rr] = p * (dpt[rr] - del) * grad;
           }
-          dpt[rr] = p * (dpt[rr] - del) * grad;
+        };
+        if (cls == TILE_PARTIAL) {
+          pds(std::true_type{});
+        } else {
+          pds(std::false_type{});
         }
         const u32x4 sb0 = pack8(dpt, 0), sb1 = pack8(dpt, 8);
 #pragma unroll

@@ -34,6 +34,11 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// The value of the first active lane, held in a scalar register: tells the
+// compiler that a per-wave quantity (e.g. the wave index) is uniform.  Kept
+// in a device function so kernel bodies name no target builtin directly.
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
@@ -89,32 +94,43 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Copy rows [r0, r0 + ROWS) of a bf16 [rows][D] matrix into an LDS tile in
-// the swizzled layout, straight from memory to LDS (buffer_load ... lds, no
-// registers).  Each load instruction fills 1 KB of the tile, lane l writing
-// bytes 16 l .. 16 l + 15, so lane l fetches the global chunk that the
-// swizzle places there.  Rows past the end of the buffer read as zeros.
-// All 4 waves of the workgroup call it; each issues ROWS * D / 2048 loads.
+// Buffer resource over rows [r0, n_rows) of a row-major matrix with
+// `row_bytes` bytes per row: offset 0 is the start of row r0, and offsets at
+// or past row n_rows read as zeros.  r0 is wave-uniform, so the resource is
+// built with scalar instructions and per-lane offsets stay loop-invariant.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int n_rows, int r0, int row_bytes) {
+  r0 = __builtin_amdgcn_readfirstlane(r0);
+  const int left = n_rows > r0 ? n_rows - r0 : 0;
+  return make_rsrc((const char*)base + (size_t)r0 * (size_t)row_bytes, (uint32_t)left * (uint32_t)row_bytes);
+}
+
+// ROWS rows of a bf16 [rows][D] matrix into an LDS tile in the swizzled
+// layout, straight from memory to LDS (buffer_load ... lds, no registers).
+// Each load instruction fills 1 KB of the tile, lane l writing bytes
+// 16 l .. 16 l + 15, so lane l fetches the global chunk that the swizzle
+// places there.  The rows come from a rows_rsrc resource, so the per-lane
+// offsets depend only on the wave and the lane and stay loop-invariant.
+// All 4 waves of the workgroup take part, each issuing PER_WAVE loads;
+// `wave` must be wave-uniform (wave_uniform).
 template <int D, int ROWS>
-__device__ __forceinline__ void tile_to_lds(__amdgpu_buffer_rsrc_t rsrc, int r0, char* tile, int wave, int lane) {
+__device__ __forceinline__ void tile_load(__amdgpu_buffer_rsrc_t rsrc, char* tile, int wave, int lane) {
   constexpr int ROW = D * 2, PER_WAVE = ROWS * ROW / 1024 / 4;
   static_assert(PER_WAVE * 4 * 1024 == ROWS * ROW, "tile must split into 1 KB loads over 4 waves");
-  const int w = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
-    const int kb = w * PER_WAVE + i;
-    const int byte = kb * 1024 + lane * 16;
+    const int byte = (wave * PER_WAVE + i) * 1024 + lane * 16;
     const int r = byte / ROW, p = (byte % ROW) / 16;
-    const uint32_t off = (uint32_t)(((r0 + r) * D + swz<D>(r, p) * 8) * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(tile + kb * 1024), 16,
-                                              off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(tile + (wave * PER_WAVE + i) * 1024), 16,
+        (uint32_t)(r * ROW + swz<D>(r, p) * 16), 0, 0, 0);
   }
 }
 
-// 64 int32 values (e.g. document ids of a key tile) into LDS by one wave.
-__device__ __forceinline__ void ints_to_lds(__amdgpu_buffer_rsrc_t rsrc, int i0, int* dst, int lane) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)dst, 4,
-                                            (uint32_t)((i0 + lane) * 4), 0, 0, 0);
+// 64 int32 values src[i0 .. i0 + 63] (zeros at or past index n) into LDS by
+// one wave.
+__device__ __forceinline__ void ints_to_lds(const void* src, int n, int i0, int* dst, int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(src, n, i0, 4), (__attribute__((address_space(3))) void*)dst, 4,
+                                            (uint32_t)(lane * 4), 0, 0, 0);
 }
 
 // Wait until every load this wave issued has landed (vmcnt = 0).

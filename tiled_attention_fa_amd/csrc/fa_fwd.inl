@@ -61,7 +61,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   decode_work(blockIdx.x, a.B, a.Hq, a.Hkv, a.n_qt, MASK == MASK_CAUSAL || MASK == MASK_DOCUMENT, b,
               hq, qt);
   const int hk = hq / a.G;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = wave_uniform(tid >> 6);  // uniform: per-wave branches stay scalar
   const int Sq = a.Sq, Skv = a.Skv;
   const int q0 = qt * kTileQ;
   const int qw0 = q0 + wave * 32;
@@ -128,15 +129,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // ---- tile loads.  bf16: straight from memory into an LDS stage (buffer
   // loads, zero past Skv).  fp32: through registers into the single stage.
-  __amdgpu_buffer_rsrc_t rsK = make_rsrc(K, (uint32_t)Skv * D * (uint32_t)sizeof(elem_t));
-  __amdgpu_buffer_rsrc_t rsV = make_rsrc(V, (uint32_t)Skv * D * (uint32_t)sizeof(elem_t));
-  __amdgpu_buffer_rsrc_t rsD = make_rsrc(doc, MASK == MASK_DOCUMENT ? (uint32_t)Skv * 4 : 0u);
   auto issue = [&](int k0, char* ks, char* vs, int* ds) {
     if constexpr (!F32) {
-      tile_to_lds<D, BN>(rsK, k0, ks, wave, lane);
-      tile_to_lds<D, BN>(rsV, k0, vs, wave, lane);
+      tile_load<D, BN>(rows_rsrc(K, Skv, k0, D * 2), ks, wave, lane);
+      tile_load<D, BN>(rows_rsrc(V, Skv, k0, D * 2), vs, wave, lane);
       if constexpr (MASK == MASK_DOCUMENT) {
-        if (wave == 0) ints_to_lds(rsD, k0, ds, lane);
+        if (wave == 0) ints_to_lds(doc, Skv, k0, ds, lane);
       }
     }
   };
@@ -267,13 +265,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
       const float alpha = fast_exp2(m - m_use);
       // ---- probabilities, row sum
+      // Plain tiles still hold raw scores; the others are already in log2 units.
+      const float mult = plain ? a.scale_log2 : 1.0f;
       float ps = 0.0f;
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = plain ? fast_exp2(__builtin_fmaf(st[t][r], a.scale_log2, -m_use))
-                                : fast_exp2(st[t][r] - m_use);
+          const float p = fast_exp2(__builtin_fmaf(st[t][r], mult, -m_use));
           st[t][r] = p;
           ps += p;
         }
