@@ -98,10 +98,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // `row_bytes` bytes per row: offset 0 is the start of row r0, and offsets at
 // or past row n_rows read as zeros.  r0 is wave-uniform, so the resource is
 // built with scalar instructions and per-lane offsets stay loop-invariant.
+// `base` must be held in scalar registers (see uniform_ptr).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int n_rows, int r0, int row_bytes) {
   r0 = __builtin_amdgcn_readfirstlane(r0);
   const int left = n_rows > r0 ? n_rows - r0 : 0;
   return make_rsrc((const char*)base + (size_t)r0 * (size_t)row_bytes, (uint32_t)left * (uint32_t)row_bytes);
+}
+
+// A wave-uniform pointer moved to scalar registers.  Pointers derived from
+// values the compiler computes in vector registers (e.g. a head index from
+// an integer division) would otherwise make it wrap each buffer load in a
+// per-lane loop; apply once, outside the loops.
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (const T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 // ROWS rows of a bf16 [rows][D] matrix into an LDS tile in the swizzled
@@ -110,12 +123,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, in
 // 16 l .. 16 l + 15, so lane l fetches the global chunk that the swizzle
 // places there.  The rows come from a rows_rsrc resource, so the per-lane
 // offsets depend only on the wave and the lane and stay loop-invariant.
-// All 4 waves of the workgroup take part, each issuing PER_WAVE loads;
+// All NW waves of the workgroup take part, each issuing PER_WAVE loads;
 // `wave` must be wave-uniform (wave_uniform).
-template <int D, int ROWS>
+template <int D, int ROWS, int NW = 4>
 __device__ __forceinline__ void tile_load(__amdgpu_buffer_rsrc_t rsrc, char* tile, int wave, int lane) {
-  constexpr int ROW = D * 2, PER_WAVE = ROWS * ROW / 1024 / 4;
-  static_assert(PER_WAVE * 4 * 1024 == ROWS * ROW, "tile must split into 1 KB loads over 4 waves");
+  constexpr int ROW = D * 2, PER_WAVE = ROWS * ROW / 1024 / NW;
+  static_assert(PER_WAVE * NW * 1024 == ROWS * ROW, "tile must split into 1 KB loads over the waves");
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
     const int byte = (wave * PER_WAVE + i) * 1024 + lane * 16;
@@ -135,6 +148,15 @@ __device__ __forceinline__ void ints_to_lds(const void* src, int n, int i0, int*
 
 // Wait until every load this wave issued has landed (vmcnt = 0).
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Workgroup barrier without a memory fence: unlike __syncthreads it does not
+// wait for this wave's loads in flight into other LDS buffers.  The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void phase_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // ---------------------------------------------------------------- masks
 // Admissibility of (query i, key j), absolute indices.  `doc_i` / `doc_j`

@@ -391,6 +391,255 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (a.visited != nullptr && tid == 0) atomicAdd(&a.visited[(size_t)(b * a.Hq + hq) * a.n_qt + qt], visited);
 }
 
+// ---------------------------------------------------------------- ping-pong forward
+// bf16, analytic masks (none, causal, sliding window), every score modifier.
+// Workgroup: 8 waves in two groups of 4 over 256 query rows; group g owns
+// rows [q0 + 128 g, q0 + 128 g + 128), 32 per wave, and both groups walk the
+// same key tiles, held once in LDS for all 8 waves.  Each SIMD hosts one wave
+// of each group and the groups run half a step apart:
+//   phase 2j:   group 0: O += V_{j-1}^T P_{j-1} and S_j = K_j Q^T (MFMA)
+//               group 1: softmax of S_{j-1} (VALU, exp)
+//   phase 2j+1: group 0: softmax of S_j;  group 1: the MFMA work of step j
+// separated by workgroup barriers, so the exponentials of one wave overlap
+// the matrix products of the other wave on the same SIMD: the warpgroup
+// ping-pong of the "FlashAttention-3 (KO)" page (intra-consumer overlap of
+// softmax and GEMM), built from the one workgroup barrier of CDNA.  Every
+// wave runs the same sequence (MFMA work of step j, barrier, softmax of
+// step j, barrier); group 1 passes one extra barrier first and group 0 one
+// at the end, which puts the groups half a step apart without a group-
+// dependent code path (two such paths double the live registers).
+// LDS: two K slots and two V slots.  Group 0 issues K_{j+1} and V_j at the
+// start of its phase 2j (into the slots that steps j-1 and j-2 no longer
+// use) and waits for them at the end of phase 2j+1.
+template <int D, int MASK, int MOD>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_pp_kernel(FwdArgs a) {
+  static_assert(MASK != MASK_DOCUMENT, "document masks take fwd_kernel");
+  constexpr int BN = 64, NT = 2, ROW = D * 2, TILE = BN * ROW;
+  constexpr int DT = D / 32, KC = D / 16;
+  constexpr int QT = 2 * kTileQ;  // query rows per workgroup
+  __shared__ __attribute__((aligned(16))) char sK0[TILE], sK1[TILE], sV0[TILE], sV1[TILE];
+
+  int b, hq, qt;
+  decode_work(blockIdx.x, a.B, a.Hq, a.Hkv, (a.Sq + QT - 1) / QT, MASK == MASK_CAUSAL, b, hq, qt);
+  const int hk = hq / a.G;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = wave_uniform(tid >> 6), grp = wave >> 2;
+  const int Sq = a.Sq, Skv = a.Skv, window = a.mask.window;
+  const int q0 = qt * QT, qg0 = q0 + kTileQ * grp, qw0 = qg0 + 32 * (wave & 3), qi = qw0 + l32;
+  const bool row_ok = qi < Sq;
+
+  const uint16_t* Q = (const uint16_t*)a.q + (size_t)(b * a.Hq + hq) * Sq * D;
+  const uint16_t* K = uniform_ptr((const uint16_t*)a.k + (size_t)(b * a.Hkv + hk) * Skv * D);
+  const uint16_t* V = uniform_ptr((const uint16_t*)a.v + (size_t)(b * a.Hkv + hk) * Skv * D);
+  const float slope = head_slope<MOD>(a.mod, hq, a.Hq);
+
+  u32x4 qf[KC];
+  {
+    const u32x4* src = (const u32x4*)(Q + (size_t)(row_ok ? qi : 0) * D);
+#pragma unroll
+    for (int c = 0; c < KC; ++c) qf[c] = row_ok ? src[2 * c + hh] : u32x4{0, 0, 0, 0};
+  }
+
+  // Key steps of the whole workgroup (union of both groups' ranges).
+  int step_lo = 0, n_steps = 0;
+  {
+    int lo, hi;
+    key_range<MASK>(q0, min(q0 + QT, Sq), Skv, window, lo, hi);
+    if (hi > lo) {
+      step_lo = lo / BN;
+      n_steps = (hi + BN - 1) / BN - step_lo;
+    }
+  }
+  auto wave_class = [&](int j) __attribute__((always_inline)) -> int {
+    if (qw0 >= Sq) return TILE_EMPTY;
+    return block_class<MASK>(qw0, 32, (step_lo + j) * BN, BN, Skv, window);
+  };
+  // Tile loads are issued by the 4 waves of group 0.
+  auto issue_k = [&](int j, char* ks) { tile_load<D, BN>(rows_rsrc(K, Skv, (step_lo + j) * BN, ROW), ks, wave & 3, lane); };
+  auto issue_v = [&](int j, char* vs) { tile_load<D, BN>(rows_rsrc(V, Skv, (step_lo + j) * BN, ROW), vs, wave & 3, lane); };
+
+  float m = kNegInf, l = 0.0f;  // running max (log2 units), this lane's partial row sum
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+  f32x16 st[NT];
+  u32x4 pb[NT][2];
+  int cls_s = TILE_EMPTY;  // class of the step whose scores / probabilities are held
+  const int gi = lane & 15, g16 = (lane >> 4) & 1;
+
+  // MFMA work of step j: O^T += V_{j-1}^T P_{j-1}^T, then S_j^T = K_j Q^T.
+  auto m_phase = [&](int j, const char* ks, const char* vs) __attribute__((always_inline)) {
+    if (cls_s != TILE_EMPTY) {
+      const int half = (gi & 1) * 8;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int ch = 4 * dt + 2 * g16 + ((gi & 3) >> 1);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const int r0 = 32 * t + 16 * cc + 4 * hh + (gi >> 2), r1 = r0 + 8;
+            const u32x2 lo = lds_read_tr16(vs + r0 * ROW + swz<D>(r0, ch) * 16 + half);
+            const u32x2 hi = lds_read_tr16(vs + r1 * ROW + swz<D>(r1, ch) * 16 + half);
+            acc[dt] = mfma_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[t][cc], acc[dt]);
+          }
+      }
+      constexpr int NM = DT * NT * 2;
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+      for (int i = 0; i < NM - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+    }
+    cls_s = j < n_steps ? wave_class(j) : TILE_EMPTY;
+    if (cls_s != TILE_EMPTY) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) st[t] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int r = 32 * t + l32;
+          st[t] = mfma_bf16(*(const u32x4*)(ks + r * ROW + swz<D>(r, 2 * c + hh) * 16), qf[c], st[t]);
+        }
+      constexpr int NM = KC * NT;
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < NM - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+  };
+
+  // Softmax of step j's scores: running max, rescale of O, P packed to bf16.
+  auto v_phase = [&](int j) __attribute__((always_inline)) {
+    if (j < 0 || j >= n_steps || cls_s == TILE_EMPTY) return;
+    const int k0 = (step_lo + j) * BN;
+    float mb = kNegInf;
+    const bool plain = (MOD == MOD_NONE) && cls_s == TILE_FULL;
+    if (plain) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mb = fmaxf(mb, st[t][r]);
+      mb = mb * a.scale_log2;
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j2 = k0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+          float x;
+          if constexpr (MOD == MOD_NONE) {
+            x = st[t][r] * a.scale_log2;
+          } else {
+            x = apply_mod<MOD>(st[t][r] * a.scale, qi, j2, slope, a.mod) * kLog2e;
+          }
+          if (cls_s == TILE_PARTIAL) {
+            const bool ok = j2 < Skv && mask_ok<MASK>(qi, j2, window, 0, 0);
+            x = ok ? x : kNegInf;
+          }
+          st[t][r] = x;
+          mb = fmaxf(mb, x);
+        }
+    }
+    mb = half_swap_max(mb);
+    const float m_new = fmaxf(m, mb);
+    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    // Plain tiles still hold raw scores; the others are already in log2 units.
+    const float mult = plain ? a.scale_log2 : 1.0f;
+    float ps = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(__builtin_fmaf(st[t][r], mult, -m_use));
+        st[t][r] = p;
+        ps += p;
+      }
+    l = l * alpha + ps;
+    m = m_new;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+        pb[t][cc] = u32x4{pack_bf16(st[t][8 * cc + 0], st[t][8 * cc + 1]), pack_bf16(st[t][8 * cc + 2], st[t][8 * cc + 3]),
+                          pack_bf16(st[t][8 * cc + 4], st[t][8 * cc + 5]), pack_bf16(st[t][8 * cc + 6], st[t][8 * cc + 7])};
+  };
+
+  // Step j of this wave.  (kc: K_j, vp: V_{j-1}; kn, vc: where K_{j+1}, V_j go.)
+  auto step = [&](int j, const char* kc, const char* vp, char* kn, char* vc) __attribute__((always_inline)) {
+    if (grp == 0) {
+      if (j + 1 < n_steps) issue_k(j + 1, kn);
+      if (j < n_steps) issue_v(j, vc);
+    }
+    m_phase(j, kc, vp);
+    phase_barrier();
+    v_phase(j);
+    wait_loads();
+    phase_barrier();
+  };
+
+  if (grp == 0 && n_steps > 0) issue_k(0, sK0);
+  wait_loads();
+  __syncthreads();
+  if (grp == 1) phase_barrier();
+  for (int j = 0; j <= n_steps; j += 2) {
+    step(j, sK0, sV1, sK1, sV0);
+    if (j + 1 <= n_steps) step(j + 1, sK1, sV0, sK0, sV1);
+  }
+  if (grp == 0) phase_barrier();
+
+  // ---- epilogue: O = acc / l, LSE = ln 2 (m + log2 l)
+  const float lt = half_swap_sum(l);
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  if (row_ok) {
+    uint16_t* Orow = (uint16_t*)a.o + ((size_t)(b * a.Hq + hq) * Sq + qi) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d0 = 32 * dt + 8 * rq + 4 * hh;
+        *(u32x2*)(Orow + d0) = u32x2{pack_bf16(acc[dt][4 * rq + 0] * inv, acc[dt][4 * rq + 1] * inv),
+                                     pack_bf16(acc[dt][4 * rq + 2] * inv, acc[dt][4 * rq + 3] * inv)};
+      }
+    if (a.lse != nullptr && hh == 0)
+      a.lse[(size_t)(b * a.Hq + hq) * Sq + qi] = lt > 0.0f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
+  }
+  // Debug count per 128-row query tile: key steps holding an admissible pair.
+  if (a.visited != nullptr && (tid & 255) == 0 && qg0 < Sq) {
+    int vis = 0;
+    for (int j = 0; j < n_steps; ++j) {
+      const int k0 = (step_lo + j) * BN;
+      if (k0 < Skv && block_class<MASK>(qg0, min(kTileQ, Sq - qg0), k0, BN, Skv, window) != TILE_EMPTY) ++vis;
+    }
+    atomicAdd(&a.visited[(size_t)(b * a.Hq + hq) * a.n_qt + qg0 / kTileQ], vis);
+  }
+}
+
+template <int D, int MASK>
+static hipError_t launch_pp(const FwdArgs& a, int mod, hipStream_t st) {
+  const dim3 grid((unsigned)(a.B * a.Hq * ((a.Sq + 2 * kTileQ - 1) / (2 * kTileQ)))), block(512);
+  switch (mod) {
+    case MOD_NONE: hipLaunchKernelGGL((fwd_pp_kernel<D, MASK, MOD_NONE>), grid, block, 0, st, a); break;
+    case MOD_ALIBI: hipLaunchKernelGGL((fwd_pp_kernel<D, MASK, MOD_ALIBI>), grid, block, 0, st, a); break;
+    case MOD_SOFTCAP: hipLaunchKernelGGL((fwd_pp_kernel<D, MASK, MOD_SOFTCAP>), grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL((fwd_pp_kernel<D, MASK, MOD_BOOST>), grid, block, 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
 template <int D, bool F32, int MASK, bool BM>
 static hipError_t launch_mod(const FwdArgs& a, int mod, hipStream_t st) {
   const dim3 grid((unsigned)(a.B * a.Hq * a.n_qt)), block(256);
@@ -405,8 +654,9 @@ static hipError_t launch_mod(const FwdArgs& a, int mod, hipStream_t st) {
 
 template <int D, bool F32, int MASK>
 static hipError_t launch_bm(const FwdArgs& a, int mod, hipStream_t st) {
-  return a.bm.tile_state != nullptr ? launch_mod<D, F32, MASK, true>(a, mod, st)
-                                    : launch_mod<D, F32, MASK, false>(a, mod, st);
+  if (a.bm.tile_state != nullptr) return launch_mod<D, F32, MASK, true>(a, mod, st);
+  if constexpr (!F32 && MASK != MASK_DOCUMENT) return launch_pp<D, MASK>(a, mod, st);
+  return launch_mod<D, F32, MASK, false>(a, mod, st);
 }
 
 template <int D, bool F32>
