@@ -90,3 +90,34 @@ def test_visited_with_block_mask(case):
             want = sum(sum(1 for s0 in range(kt * 128, kt * 128 + 128, step) if s0 < Skv) for kt in lists[qt])
             for h in range(H):
                 assert int(vis[b, h, qt]) == want
+
+
+def _unsorted_ids(pattern, B, S, seed):
+    rng = np.random.default_rng(seed)
+    if pattern == "random":  # ids drawn per token from a small alphabet
+        ids = rng.integers(0, 4, size=(B, S))
+    else:  # 128-token blocks alternating {0 | 2} halves with blocks of id 1
+        blk = np.arange(S) // 128
+        ids = np.where(blk % 2 == 0, np.where(np.arange(S) % 128 < 64, 0, 2), 1)
+        ids = np.broadcast_to(ids, (B, S)).copy()
+        ids[:, rng.integers(0, S)] = 5  # one stray id
+    return torch.from_numpy(ids.astype(np.int32))
+
+
+@pytest.mark.parametrize("pattern", ["random", "interleaved"])
+def test_builder_unsorted_doc_ids(pattern):
+    """Document ids need not be sorted: blocks whose id ranges overlap without
+    a common id must come out EMPTY, found by the pair check."""
+    B, S = 2, 1100
+    doc = _unsorted_ids(pattern, B, S, 90)
+    bm = fa.build_block_mask(3, B, S, S, doc_ids=dev(doc))
+    torch.cuda.synchronize()
+    st, kvl, ql = oracle.tile_states(oracle.Variant(mask=3, doc_ids=doc.numpy()), B, S, S, 128, 128)
+    assert np.array_equal(bm.tile_state.cpu().numpy(), st)
+    kc, ki = bm.kv_count.cpu().numpy(), bm.kv_index.cpu().numpy()
+    for b in range(B):
+        for t in range(st.shape[1]):
+            n = len(kvl[b][t])
+            assert kc[b, t] == n and np.array_equal(ki[b, t, :n], kvl[b][t])
+    if pattern == "interleaved":  # the case the id ranges alone cannot decide
+        assert (st == 0).sum() > 0 and (st == 1).sum() > 0
