@@ -114,6 +114,15 @@ typedef struct {
   int32_t* kv_index;         /* [n_b][n_q][n_kv] ascending, first kv_count valid */
   int32_t* q_count;          /* [n_b][n_kv] non-empty q tiles per kv tile */
   int32_t* q_index;          /* [n_b][n_kv][n_q] ascending, first q_count valid */
+  int32_t* q_order;          /* [n_b][n_q] or NULL: the q tiles by descending kv_count
+                                (ties by ascending index).  The query-stationary
+                                kernels start their tiles in this order, longest
+                                first, so the hardware's in-order dispatch to free
+                                compute units balances uneven rows (document
+                                masks).  Rows of more than 2048 tiles get the
+                                identity order.  NULL: the default order. */
+  int32_t* kv_order;         /* [n_b][n_kv] or NULL: the kv tiles by descending
+                                q_count, for the key-stationary dK/dV kernel */
 } fa_block_mask;
 
 /* Forward pass.  q, k, v, out: device, dtype elements in the layout above.
@@ -168,9 +177,10 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq, int D);
 
 /* Build a block mask for (mask_kind, mask_params, B, Sq, Skv) into the
  * caller's arrays described by *out (block sizes, n_q, n_kv, n_b and the five
- * pointers must be set; n_b must be B for FA_MASK_DOCUMENT and may be 1
- * otherwise).  One stream-ordered pass; every entry of every array is
- * written (unused list slots are set to -1). */
+ * list pointers must be set; q_order and kv_order are filled when not NULL;
+ * n_b must be B for FA_MASK_DOCUMENT and may be 1 otherwise).  One
+ * stream-ordered pass; every entry of every array is written (unused list
+ * slots are set to -1). */
 int fa_block_mask_build(int mask_kind, const fa_mask_params* mask_params,
                         int B, int Sq, int Skv, const fa_block_mask* out, void* stream);
 

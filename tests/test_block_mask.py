@@ -47,6 +47,17 @@ def test_builder_matches_brute_force(case):
         for t in range(st.shape[2]):
             n = len(ql[b][t])
             assert qc[b, t] == n and np.array_equal(qi[b, t, :n], ql[b][t]) and np.all(qi[b, t, n:st.shape[1]] == -1)
+    _check_orders(bm, kc, qc)
+
+
+def _check_orders(bm, kc, qc):
+    """q_order / kv_order: the tiles by descending list length, ties by index."""
+    for order, cnt in ((bm.q_order, kc), (bm.kv_order, qc)):
+        o = order.cpu().numpy()
+        for b in range(cnt.shape[0]):
+            n = cnt.shape[1]
+            want = sorted(range(n), key=lambda t: (-int(cnt[b, t]), t))
+            assert np.array_equal(o[b, :n], want)
 
 
 def test_doc_config_shape_mask():
@@ -119,5 +130,24 @@ def test_builder_unsorted_doc_ids(pattern):
         for t in range(st.shape[1]):
             n = len(kvl[b][t])
             assert kc[b, t] == n and np.array_equal(ki[b, t, :n], kvl[b][t])
+    _check_orders(bm, kc, bm.q_count.cpu().numpy())
     if pattern == "interleaved":  # the case the id ranges alone cannot decide
         assert (st == 0).sum() > 0 and (st == 1).sum() > 0
+
+
+@pytest.mark.parametrize("mask", [1, 3])
+def test_orders_change_nothing_but_schedule(mask):
+    """Forward and backward results are bit-identical with and without the
+    longest-first tile orders (only the workgroup-to-tile map changes)."""
+    B, H, S, D = 2, 2, 900, 128
+    q, k, v = (dev(t) for t in synth.qkv(B, H, H, S, S, D, 77))
+    do = dev(synth.randn((B, H, S, D), 78))
+    doc = _docs(B, S, 79, lo=50, hi=400) if mask == 3 else None
+    res = []
+    for orders in (True, False):
+        bm = fa.build_block_mask(mask, B, S, S, doc_ids=dev(doc), orders=orders)
+        o, lse = fa.forward(q, k, v, mask=mask, doc_ids=dev(doc), block_mask=bm, return_lse=True)
+        res.append((o, lse) + tuple(fa.backward(q, k, v, o, do, lse, mask=mask, doc_ids=dev(doc), block_mask=bm)))
+    torch.cuda.synchronize()
+    for x, y in zip(*res):
+        assert torch.equal(x, y)

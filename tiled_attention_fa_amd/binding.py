@@ -44,7 +44,8 @@ class FaBlockMask(ctypes.Structure):
                 ("n_q", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("n_b", ctypes.c_int32),
                 ("tile_state", ctypes.c_void_p), ("kv_count", ctypes.c_void_p),
                 ("kv_index", ctypes.c_void_p), ("q_count", ctypes.c_void_p),
-                ("q_index", ctypes.c_void_p)]
+                ("q_index", ctypes.c_void_p), ("q_order", ctypes.c_void_p),
+                ("kv_order", ctypes.c_void_p)]
 
 
 class FaError(RuntimeError):
@@ -167,7 +168,7 @@ def _params(mask, window, doc_ids, visited, mod, alibi_slopes, softcap, boost_ra
 class BlockMask:
     """Device arrays of a 128 x 128 block mask (owned by torch tensors)."""
 
-    def __init__(self, n_b, n_q, n_kv, device):
+    def __init__(self, n_b, n_q, n_kv, device, orders=True):
         torch = _torch()
         self.n_b, self.n_q, self.n_kv = n_b, n_q, n_kv
         self.tile_state = torch.empty((n_b, n_q, n_kv), dtype=torch.uint8, device=device)
@@ -175,18 +176,24 @@ class BlockMask:
         self.kv_index = torch.empty((n_b, n_q, max(n_kv, 1)), dtype=torch.int32, device=device)
         self.q_count = torch.empty((n_b, n_kv), dtype=torch.int32, device=device)
         self.q_index = torch.empty((n_b, max(n_kv, 1), max(n_q, 1)), dtype=torch.int32, device=device)
+        # longest-first tile orders (optional in the C struct)
+        self.q_order = torch.empty((n_b, max(n_q, 1)), dtype=torch.int32, device=device) if orders else None
+        self.kv_order = torch.empty((n_b, max(n_kv, 1)), dtype=torch.int32, device=device) if orders else None
 
     def struct(self) -> FaBlockMask:
+        ptr = lambda t: None if t is None else t.data_ptr()
         return FaBlockMask(BLOCK, BLOCK, self.n_q, self.n_kv, self.n_b,
                            self.tile_state.data_ptr(), self.kv_count.data_ptr(), self.kv_index.data_ptr(),
-                           self.q_count.data_ptr(), self.q_index.data_ptr())
+                           self.q_count.data_ptr(), self.q_index.data_ptr(), ptr(self.q_order),
+                           ptr(self.kv_order))
 
 
 def build_block_mask(mask: int, B: int, Sq: int, Skv: int, *, window: int = 0, doc_ids=None,
-                     device="cuda", stream=None, into: BlockMask | None = None) -> BlockMask:
-    """Build (or rebuild ``into``, allocating nothing) the block mask of a mask kind."""
+                     device="cuda", stream=None, into: BlockMask | None = None, orders: bool = True) -> BlockMask:
+    """Build (or rebuild ``into``, allocating nothing) the block mask of a mask kind;
+    ``orders`` adds the longest-first tile orders the kernels schedule by."""
     n_b = B if mask == MASK_DOCUMENT else 1
-    bm = into if into is not None else BlockMask(n_b, -(-Sq // BLOCK), -(-Skv // BLOCK), device)
+    bm = into if into is not None else BlockMask(n_b, -(-Sq // BLOCK), -(-Skv // BLOCK), device, orders)
     mp, _ = _params(mask, window, doc_ids, None, MOD_NONE, None, 0.0, 0, 1.0)
     s = bm.struct()
     rc = fa_block_mask_build(int(mask), ctypes.byref(mp), int(B), int(Sq), int(Skv), ctypes.byref(s), _stream(stream))

@@ -81,7 +81,7 @@ int check_variant(int B, int Hq, int Sq, int Skv, float scale, int mask_kind, co
 
 int check_block_mask(const fa_block_mask* bm, int mask_kind, int B, int Sq, int Skv, bool need_q_lists,
                      BlockMaskArgs& out) {
-  out = BlockMaskArgs{nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 0};
+  out = BlockMaskArgs{nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, nullptr, nullptr};
   if (!bm) return FA_OK;
   if (bm->block_q != kMaskBlock || bm->block_kv != kMaskBlock) return FA_ERR_UNSUPPORTED;
   if (bm->n_q != cdiv(Sq, kMaskBlock) || bm->n_kv != cdiv(Skv, kMaskBlock)) return FA_ERR_SHAPE;
@@ -91,8 +91,9 @@ int check_block_mask(const fa_block_mask* bm, int mask_kind, int B, int Sq, int 
   if (need_q_lists && (!bm->q_count || !bm->q_index)) return FA_ERR_NULL;
   if (!aligned(bm->kv_count, 4) || !aligned(bm->kv_index, 4)) return FA_ERR_ALIGN;
   if (need_q_lists && (!aligned(bm->q_count, 4) || !aligned(bm->q_index, 4))) return FA_ERR_ALIGN;
+  if (!aligned(bm->q_order, 4) || !aligned(bm->kv_order, 4)) return FA_ERR_ALIGN;
   out = BlockMaskArgs{bm->tile_state, bm->kv_count, bm->kv_index, bm->q_count, bm->q_index,
-                      bm->n_b, bm->n_q, bm->n_kv};
+                      bm->n_b, bm->n_q, bm->n_kv, bm->q_order, bm->kv_order};
   return FA_OK;
 }
 

@@ -16,6 +16,7 @@
 // writes the non-empty tiles in ascending order.
 // Kernel 2: one workgroup per (batch row, key tile), one thread per query
 // tile; a prefix sum writes the ascending list of non-empty query tiles.
+// Kernel 3 (when the caller asks for them): the longest-first tile orders.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -216,6 +217,39 @@ __global__ __launch_bounds__(256) void block_mask_cols_kernel(BlockMaskArgs m) {
   if (tid == 0) m.q_count[bb * m.n_kv + kt] = count;
 }
 
+// Kernel 3: for each batch row, the q tiles by descending kv_count (grid
+// y = 0) and the kv tiles by descending q_count (y = 1), ties by ascending
+// index: item t goes to position #{u : c[u] > c[t] or (c[u] == c[t] and
+// u < t)}, a permutation, so every position is written exactly once.
+// Rows of more tiles than this (sequences over 256K tokens) get the identity
+// order: the quadratic ranking below would cost more than it balances.
+constexpr int kOrderMax = 2048;
+
+__global__ __launch_bounds__(256) void block_mask_order_kernel(BlockMaskArgs m) {
+  const int bb = blockIdx.x, which = blockIdx.y;
+  const int n = which == 0 ? m.n_q : m.n_kv;
+  const int32_t* c = which == 0 ? m.kv_count + (size_t)bb * m.n_q : m.q_count + (size_t)bb * m.n_kv;
+  int32_t* order = which == 0 ? m.q_order : m.kv_order;
+  if (order == nullptr) return;
+  order += (size_t)bb * n;
+  if (n > kOrderMax) {
+    for (int t = threadIdx.x; t < n; t += 256) order[t] = t;
+    return;
+  }
+  __shared__ int sc[kOrderMax];  // the counts, read once
+  for (int t = threadIdx.x; t < n; t += 256) sc[t] = c[t];
+  __syncthreads();
+  for (int t = threadIdx.x; t < n; t += 256) {
+    const int ct = sc[t];
+    int pos = 0;
+    for (int u = 0; u < n; ++u) {
+      const int cu = sc[u];
+      pos += (cu > ct) | ((cu == ct) & (u < t));
+    }
+    order[pos] = t;
+  }
+}
+
 hipError_t launch_block_mask(int mask_kind, int window, const int32_t* doc_ids, int Sq, int Skv,
                              const BlockMaskArgs& m, hipStream_t st) {
   if (m.n_q > 0) {
@@ -226,6 +260,11 @@ hipError_t launch_block_mask(int mask_kind, int window, const int32_t* doc_ids, 
   }
   if (m.n_kv > 0) {
     hipLaunchKernelGGL(block_mask_cols_kernel, dim3((unsigned)m.n_kv, (unsigned)m.n_b), dim3(256), 0, st, m);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if ((m.q_order != nullptr || m.kv_order != nullptr) && (m.n_q > 0 || m.n_kv > 0)) {
+    hipLaunchKernelGGL(block_mask_order_kernel, dim3((unsigned)m.n_b, 2u), dim3(256), 0, st, m);
     return hipGetLastError();
   }
   return hipSuccess;

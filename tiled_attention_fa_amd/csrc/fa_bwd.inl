@@ -97,6 +97,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   int b, hk, kt;
   decode_work(blockIdx.x, a.B, a.Hkv, a.Hkv, a.n_kt, false, b, hk, kt);
+  if constexpr (BM) kt = ordered_tile(a.bm.kv_order, a.bm.n_b, b, a.bm.n_kv, kt, kt);
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave = wave_uniform(tid >> 6);  // uniform: per-wave branches stay scalar
   const int gi = lane & 15, g16 = (lane >> 4) & 1;
@@ -310,8 +311,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(16))) int sD0[BN], sD1[BN];
 
   int b, hq, qt;
-  decode_work(blockIdx.x, a.B, a.Hq, a.Hkv, a.n_qt, MASK == MASK_CAUSAL || MASK == MASK_DOCUMENT, b, hq,
-              qt);
+  decode_work(blockIdx.x, a.B, a.Hq, a.Hkv, a.n_qt,
+              (MASK == MASK_CAUSAL || MASK == MASK_DOCUMENT) && !(BM && a.bm.q_order), b, hq, qt);
+  if constexpr (BM) qt = ordered_tile(a.bm.q_order, a.bm.n_b, b, a.bm.n_q, qt, qt);
   const int hk = hq / a.G;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave = wave_uniform(tid >> 6);  // uniform: per-wave branches stay scalar

@@ -263,4 +263,12 @@ __device__ __forceinline__ void decode_work(int P, int B, int Hq, int Hkv, int n
   tile = heavy_first ? (n_tiles - 1 - r) : r;
 }
 
+// Tile at position r of a block mask's longest-first order, or `fallback`
+// when the mask carries no order.  The entry is clamped into [0, n).
+__device__ __forceinline__ int ordered_tile(const int32_t* order, int n_b, int b, int n, int r, int fallback) {
+  if (order == nullptr) return fallback;
+  const int v = order[(size_t)(n_b == 1 ? 0 : b) * n + r];
+  return min(max(v, 0), n - 1);
+}
+
 }  // namespace miattn
