@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd/bwd TFLOPS (unmasked FLOPs) + % of bf16 MFMA peak, S=8192 D=128"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_FP8_TFLOPS = 5033.2    # 256 CU x 2.4 GHz x 8192 dense fp8 flop/clk/CU
 PEAK_HBM_GBS = 8000.0
 MASK_NAMES = {0: "none", 1: "causal", 2: "sliding_window", 3: "document"}
 MOD_NAMES = {0: "none", 1: "alibi", 2: "softcap", 3: "local_boost"}
@@ -78,6 +79,8 @@ def cpu_baseline(w, heads: int):
     from tiled_attention_fa_amd.binding import default_scale
     scale = default_scale(w.D)
     G = w.Hq // w.Hkv
+    if w.dtype == "fp8":
+        return _cpu_baseline_fp8(w, q, k, v, var, scale, max(1, heads // 16), threads)  # ~20 s a head
     todo = [(0, h) for h in range(min(heads, w.Hq))]
     t0 = time.perf_counter()
     for b, h in todo:
@@ -94,6 +97,37 @@ def cpu_baseline(w, heads: int):
             "sample": f"{'forward+backward' if w.backward else 'forward'} of {len(todo)} of {w.B * w.Hq} "
                       f"(batch, head) pairs at full S={w.S}, numpy float64 with {threads} BLAS threads; "
                       f"value = admissible-pair FLOPs of that sample / its time"}
+
+
+def _cpu_baseline_fp8(w, q, k, v, var, scale, heads, threads):
+    """The FP8 oracle (quantization and the FP8 forward emulation, numpy
+    float64) on `heads` whole heads, rows in chunks of 2048."""
+    import numpy as np
+    import torch
+
+    import synth
+    from oracle import fp8 as ofp8
+    from tiled_attention_fa_amd import flops
+
+    s = synth.signs(w.D, synth.FP8_SIGN_SEED).numpy()
+
+    def f64(t):
+        return t.to(torch.float64).numpy()
+    t0 = time.perf_counter()
+    for h in range(heads):
+        hk = h // (w.Hq // w.Hkv)
+        q8, qs = ofp8.block_quantize(f64(q[0, h])[None], s)
+        k8, ks = ofp8.block_quantize(f64(k[0, hk])[None], s)
+        v8, vs = ofp8.block_quantize(f64(v[0, hk])[None])
+        for r0 in range(0, w.S, 2048):
+            ofp8.fp8_forward(q8, k8, v8, qs, ks, vs, scale, var, rows=np.arange(r0, min(w.S, r0 + 2048)))
+    dt = time.perf_counter() - t0
+    per_head = flops.pairs_per_row_batch(w.mask, w.S, w.S, w.window, None)
+    return {"value": per_head * heads * 4 * w.D / dt / 1e12, "unit": "TFLOPS", "cores": int(threads),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"FP8 quantization + FP8 forward emulation of {heads} of {w.B * w.Hq} (batch, head) pairs "
+                      f"at full S={w.S}, numpy float64 with {threads} BLAS threads; value = admissible-pair "
+                      f"FLOPs of that sample / its time"}
 
 
 def main():
@@ -149,11 +183,26 @@ def main():
     bm = fa.build_block_mask(w.mask, w.B, w.S, w.S, window=w.window, doc_ids=doc) if use_bm else None
 
     names = (["block_mask"] if use_bm else []) + ["fwd"] + (["bwd_delta", "bwd_dkdv", "bwd_dq"] if w.backward else [])
+    is_fp8 = w.dtype == "fp8"
+    if is_fp8:
+        # Quantized once, outside the timed region (as the FP8 tables of the
+        # pages exclude the quantization time); Q and K with incoherent processing.
+        signs = synth.signs(w.D, synth.FP8_SIGN_SEED).to(dev)
+        q8, qs = fa.quantize_fp8(q, signs)
+        k8, ks = fa.quantize_fp8(k, signs)
+        v8, vs = fa.quantize_fp8(v)
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
 
     def step(evs):
         i = 0
         if evs:
             evs[i].record(stream)
+        if is_fp8:
+            fa.forward_fp8(q8, k8, v8, qs, ks, vs, mask=w.mask, window=w.window, out=out, lse=lse,
+                           return_lse=w.lse)
+            if evs:
+                evs[1].record(stream)
+            return
         if use_bm:
             fa.build_block_mask(w.mask, w.B, w.S, w.S, window=w.window, doc_ids=doc, into=bm)
             i += 1
@@ -196,6 +245,7 @@ def main():
     # Q K^T and dO V^T repeats work the dK/dV kernel already counts).
     algo = {"fwd": f_fwd, "bwd_dkdv": 8.0 * w.D * npairs, "bwd_dq": 2.0 * w.D * npairs}
     dominant = max((n for n in names if n in algo), key=lambda n: kernel_ms[n])
+    peak = PEAK_FP8_TFLOPS if is_fp8 else PEAK_BF16_TFLOPS  # a contraction takes its own dtype's peak
     achieved = algo[dominant] / (kernel_ms[dominant] * 1e-3) / 1e12
     rec = {
         "metric": METRIC,
@@ -208,20 +258,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3"}.get(w.dtype, "f32"),
         "data": "synthetic: seeded N(0,1) tensors of the workload's shape",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D,
                    "mask": MASK_NAMES[w.mask], "mod": MOD_NAMES[w.mod], "window": w.window,
                    "pass": "fwd+bwd" if w.backward else "fwd", "lse": bool(w.lse or w.backward),
                    "admissible_pairs": npairs},
         "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        **({"pct_of_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2)} if is_fp8 else {}),
         "fwd_tflops": round(f_fwd / (kernel_ms["fwd"] * 1e-3) / 1e12, 2),
         "bwd_tflops": round(f_bwd / (sum(kernel_ms[n] for n in names if n.startswith("bwd")) * 1e-3) / 1e12, 2)
         if w.backward else None,
         "kernel_ms": {n: round(t, 4) for n, t in kernel_ms.items()},
         "wall_s": round(wall, 3),
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(w.name, dominant)},
     }
     if not args.no_cpu_baseline:

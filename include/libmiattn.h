@@ -175,6 +175,41 @@ int fa_bwd_phase(int phase, const void* q, const void* k, const void* v, const v
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq, int D);
 
+/* FP8 path ("FlashAttention-3 (KO)" page, technical innovation 3: FP8
+ * doubles the matrix throughput of 16-bit formats; incoherent processing
+ * multiplies Q and K by a random orthogonal matrix before quantizing, which
+ * spreads outliers while Q K^T is unchanged).  Format: OCP E4M3 (sign, 4
+ * exponent bits with bias 7, 3 mantissa bits, largest finite 448).  Every
+ * tensor carries one power-of-two scale per block of 128 rows of each
+ * (batch, head), stored as the byte e + 127 (E8M0): row value ~= E4M3 value
+ * * 2^e, 2^e the smallest power of two with the block's max |value| <= 448
+ * * 2^e. */
+
+/* Quantize x (bf16 [rows][S][D], rows = B * H, contiguous) to E4M3 codes x8
+ * (uint8, same layout) and scale bytes (uint8 [rows][ceil(S/128)]), rounding
+ * to nearest even.  signs: device float [D] of +-1, or NULL.  When given,
+ * each row is first replaced by (row * signs) H / sqrt(D), H the Sylvester
+ * Hadamard matrix (orthogonal, so applying the same signs to Q and K leaves
+ * Q K^T unchanged).  D in {64, 128}; x and x8 16-byte aligned.  Returns an
+ * fa_status; rows * S == 0 is a no-op. */
+int fa_fp8_quantize(const void* x, void* x8, uint8_t* scales, int rows, int S, int D, const float* signs,
+                    void* stream);
+
+/* Forward pass from E4M3 tensors: q8 [B][Hq][Sq][D], k8 and v8
+ * [B][Hkv][Skv][D] with their scale bytes (q_scale [B][Hq][ceil(Sq/128)],
+ * k_scale and v_scale [B][Hkv][ceil(Skv/128)]), as written by
+ * fa_fp8_quantize.  Writes out (bf16 [B][Hq][Sq][D]) and, if lse is not
+ * NULL, LSE (float [B][Hq][Sq], natural log).  Both products run on FP8
+ * matrix cores with float32 accumulation; the probabilities of each 64-key
+ * step are rounded to E4M3 (relative to the running row max) for the P V
+ * product, while the row sum uses them unrounded.  scale multiplies the
+ * dequantized q . k.  Masks: FA_MASK_NONE, FA_MASK_CAUSAL,
+ * FA_MASK_SLIDING_WINDOW (FA_MASK_DOCUMENT -> FA_ERR_UNSUPPORTED); no score
+ * modifier.  D in {64, 128}; tensors 16-byte aligned. */
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const uint8_t* q_scale, const uint8_t* k_scale,
+               const uint8_t* v_scale, void* out, float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int D,
+               float scale, int mask_kind, const fa_mask_params* mask_params, void* stream);
+
 /* Build a block mask for (mask_kind, mask_params, B, Sq, Skv) into the
  * caller's arrays described by *out (block sizes, n_q, n_kv, n_b and the five
  * list pointers must be set; q_order and kv_order are filled when not NULL;

@@ -96,6 +96,13 @@ class Workload:
     seed: int = 0
 
 
+def signs(D: int, seed: int) -> torch.Tensor:
+    """Seeded vector of random +-1 (float32 [D]): the diagonal of the random
+    orthogonal matrix of the FP8 path's incoherent processing."""
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randint(0, 2, (D,), generator=g) * 2 - 1).to(torch.float32)
+
+
 # The five workload families: a tiny fp32 MHA check, a causal prefill, GQA
 # with the four score-mod/mask variants, a packed document batch and a causal
 # forward+backward.  Seeds are 1000 + family index.
@@ -117,12 +124,19 @@ WORKLOADS = {
                            lse=True, doc_range=(256, 4096), seed=1003),
     "causal_fwd_bwd": Workload("causal_fwd_bwd", 2, 16, 16, 8192, 128, "bf16",
                                mask=MASK_CAUSAL, lse=True, backward=True, seed=1004),
+    # The FP8 forward (E4M3 Q, K, V; Q and K with incoherent processing) at
+    # the causal S=8192 shape.
+    "causal_fwd_fp8": Workload("causal_fwd_fp8", 2, 16, 16, 8192, 128, "fp8",
+                               mask=MASK_CAUSAL, lse=True, seed=1005),
 }
+
+FP8_SIGN_SEED = 2005  # seed of the incoherence signs of the FP8 workloads
 
 
 def workload_inputs(w: Workload, dtype: str | None = None):
-    """(q, k, v, extras) CPU tensors for a workload; extras holds dO and doc ids."""
-    dt = dtype or w.dtype
+    """(q, k, v, extras) CPU tensors for a workload; extras holds dO and doc ids.
+    FP8 workloads start from bf16 tensors (quantized by the caller)."""
+    dt = dtype or ("bf16" if w.dtype == "fp8" else w.dtype)
     q, k, v = qkv(w.B, w.Hq, w.Hkv, w.S, w.S, w.D, w.seed, dt)
     extras = {}
     if w.backward:

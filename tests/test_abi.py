@@ -144,3 +144,36 @@ def test_block_mask_build_validation():
     assert fa.fa_block_mask_build(1, None, 1, 100, 100, ctypes.byref(bad), None) == fa.FA_ERR_SHAPE
     no_q = fa.FaBlockMask(128, 128, 1, 1, 1, 0x300000, 0x300100, 0x300200, None, None)
     assert fa.fa_block_mask_build(1, None, 1, 100, 100, ctypes.byref(no_q), None) == fa.FA_ERR_NULL
+
+
+def fp8_fwd(q=P, k=P, v=P, qs=P, ks=P, vs=P, o=P, lse=None, B=1, Hq=2, Hkv=2, Sq=16, Skv=16, D=64,
+            scale=0.125, mask=0, mp=None):
+    L = fa.lib()
+    return L.fa_fwd_fp8(q, k, v, qs, ks, vs, o, lse, B, Hq, Hkv, Sq, Skv, D, scale, mask,
+                        ctypes.byref(mp) if mp else None, None)
+
+
+def test_fp8_fwd_validation():
+    assert fp8_fwd(D=96) == fa.FA_ERR_UNSUPPORTED
+    assert fp8_fwd(mask=3, mp=fa.FaMaskParams(0, 0x200000, None)) == fa.FA_ERR_UNSUPPORTED
+    assert fp8_fwd(mask=2) == fa.FA_ERR_NULL
+    assert fp8_fwd(mask=2, mp=fa.FaMaskParams(0, None, None)) == fa.FA_ERR_PARAM
+    assert fp8_fwd(Hq=3, Hkv=2) == fa.FA_ERR_SHAPE
+    assert fp8_fwd(scale=-1.0) == fa.FA_ERR_PARAM
+    assert fp8_fwd(q=None) == fa.FA_ERR_NULL
+    assert fp8_fwd(ks=None) == fa.FA_ERR_NULL
+    assert fp8_fwd(qs=None) == fa.FA_ERR_NULL
+    assert fp8_fwd(k=MIS) == fa.FA_ERR_ALIGN
+    assert fp8_fwd(lse=ctypes.c_void_p(0x100002)) == fa.FA_ERR_ALIGN
+    assert fp8_fwd(B=0, q=None, k=None, v=None, o=None, qs=None, ks=None, vs=None) == fa.FA_OK
+
+
+def test_fp8_quantize_validation():
+    L = fa.lib()
+    assert L.fa_fp8_quantize(P, P, P, 2, 16, 96, None, None) == fa.FA_ERR_UNSUPPORTED
+    assert L.fa_fp8_quantize(P, P, P, -1, 16, 64, None, None) == fa.FA_ERR_SHAPE
+    assert L.fa_fp8_quantize(None, P, P, 2, 16, 64, None, None) == fa.FA_ERR_NULL
+    assert L.fa_fp8_quantize(P, P, None, 2, 16, 64, None, None) == fa.FA_ERR_NULL
+    assert L.fa_fp8_quantize(MIS, P, P, 2, 16, 64, None, None) == fa.FA_ERR_ALIGN
+    assert L.fa_fp8_quantize(P, P, P, 2, 16, 64, ctypes.c_void_p(0x100002), None) == fa.FA_ERR_ALIGN
+    assert L.fa_fp8_quantize(None, None, None, 0, 16, 64, None, None) == fa.FA_OK

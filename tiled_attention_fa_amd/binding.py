@@ -27,7 +27,7 @@ BLOCK = 128
 FA_BWD_DELTA, FA_BWD_DKDV, FA_BWD_DQ = 1, 2, 4
 
 EXPORTED = ("fa_fwd", "fa_fwd_kv_step", "fa_bwd", "fa_bwd_phase", "fa_bwd_workspace_bytes",
-            "fa_block_mask_build", "fa_status_str", "fa_version")
+            "fa_block_mask_build", "fa_fp8_quantize", "fa_fwd_fp8", "fa_status_str", "fa_version")
 
 
 class FaMaskParams(ctypes.Structure):
@@ -88,6 +88,11 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_kv_step.restype = _I
         L.fa_version.argtypes = []
         L.fa_version.restype = _I
+        L.fa_fp8_quantize.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P]
+        L.fa_fp8_quantize.restype = _I
+        L.fa_fwd_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float,
+                                 _I, ctypes.POINTER(FaMaskParams), _P]
+        L.fa_fwd_fp8.restype = _I
         _LIB = L
     return _LIB
 
@@ -163,6 +168,47 @@ def _params(mask, window, doc_ids, visited, mod, alibi_slopes, softcap, boost_ra
     op = FaModParams(None if alibi_slopes is None else alibi_slopes.data_ptr(), float(softcap),
                      int(boost_radius), float(boost_factor))
     return mp, op
+
+
+FP8_BLOCK = 128  # rows per FP8 quantization block
+
+
+def quantize_fp8(x, signs=None, *, out=None, scales=None, stream=None):
+    """E4M3 codes and per-128-row E8M0 scale bytes of a bf16 [B, H, S, D]
+    tensor; with ``signs`` (float32 [D] of +-1) the rows are first multiplied
+    by diag(signs) H / sqrt(D) (incoherent processing)."""
+    torch = _torch()
+    B, H, S, D = x.shape
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, -(-S // FP8_BLOCK)), dtype=torch.uint8, device=x.device)
+    rc = lib().fa_fp8_quantize(_ptr(x), _ptr(out), _ptr(scales), int(B * H), int(S), int(D), _ptr(signs),
+                               _stream(stream))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_fp8_quantize")
+    return out, scales
+
+
+def forward_fp8(q8, k8, v8, q_scale, k_scale, v_scale, *, scale=None, mask=MASK_NONE, window=0,
+                return_lse=False, out=None, lse=None, stream=None):
+    """bf16 O (and LSE) from E4M3 q8 [B,Hq,Sq,D], k8/v8 [B,Hkv,Skv,D] with their
+    block scales (masks: none, causal, sliding window)."""
+    torch = _torch()
+    B, Hq, Sq, D = q8.shape
+    Hkv, Skv = k8.shape[1], k8.shape[2]
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.bfloat16, device=q8.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q8.device)
+    mp, _ = _params(mask, window, None, None, MOD_NONE, None, 0.0, 0, 1.0)
+    sc = default_scale(D) if scale is None else float(scale)
+    rc = lib().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(out),
+                          _ptr(lse), int(B), int(Hq), int(Hkv), int(Sq), int(Skv), int(D), sc, int(mask),
+                          ctypes.byref(mp), _stream(stream))
+    if rc != FA_OK:
+        raise FaError(rc, "fa_fwd_fp8")
+    return (out, lse) if return_lse else out
 
 
 class BlockMask:

@@ -182,6 +182,60 @@ static size_t ws_half(int B, int Hq, int Sq) {
   return (n + 255) & ~(size_t)255;
 }
 
+int fa_fp8_quantize(const void* x, void* x8, uint8_t* scales, int rows, int S, int D, const float* signs,
+                    void* stream) {
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  if (rows < 0 || S < 0 || S > kMaxSeq || rows > 65535) return FA_ERR_SHAPE;
+  const bool any = (long long)rows * S > 0;
+  int rc;
+  if ((rc = check_tensor(x, any)) || (rc = check_tensor(x8, any))) return rc;
+  if (any && !scales) return FA_ERR_NULL;
+  if (signs && !aligned(signs, 4)) return FA_ERR_ALIGN;
+  if (!any) return FA_OK;
+  const hipError_t e = launch_fp8_quantize(x, x8, scales, rows, S, D, signs, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const uint8_t* q_scale, const uint8_t* k_scale,
+               const uint8_t* v_scale, void* out, float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int D,
+               float scale, int mask_kind, const fa_mask_params* mask_params, void* stream) {
+  int rc = check_shapes(B, Hq, Hkv, Sq, Skv, D);
+  if (rc) return rc;
+  if (mask_kind == FA_MASK_DOCUMENT) return FA_ERR_UNSUPPORTED;
+  MaskArgs mask;
+  ModArgs mod;
+  rc = check_variant(B, Hq, Sq, Skv, scale, mask_kind, mask_params, FA_MOD_NONE, nullptr, mask, mod);
+  if (rc) return rc;
+  const bool has_q = (long long)B * Sq > 0, has_kv = (long long)B * Skv > 0;
+  if ((rc = check_tensor(q8, has_q)) || (rc = check_tensor(out, has_q)) || (rc = check_tensor(k8, has_kv)) ||
+      (rc = check_tensor(v8, has_kv)))
+    return rc;
+  if ((has_q && !q_scale) || (has_kv && (!k_scale || !v_scale))) return FA_ERR_NULL;
+  if (lse && !aligned(lse, 4)) return FA_ERR_ALIGN;
+  if (!has_q) return FA_OK;
+  Fp8FwdArgs a{};
+  a.q8 = (const uint8_t*)q8;
+  a.k8 = (const uint8_t*)k8;
+  a.v8 = (const uint8_t*)v8;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.o = out;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.Sq = Sq;
+  a.Skv = Skv;
+  a.D = D;
+  a.n_qt = (int)cdiv(Sq, kTileQ);
+  a.window = mask.window;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  const hipError_t e = launch_fp8_fwd(a, mask_kind, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq, int D) {
   (void)D;
   if (B <= 0 || Hq <= 0 || Sq <= 0) return 256;

@@ -51,6 +51,23 @@ struct FwdArgs {
   BlockMaskArgs bm;
 };
 
+// FP8 forward: E4M3 tensors with one E8M0 scale byte per 128-row block of
+// each (batch, head).
+struct Fp8FwdArgs {
+  const uint8_t* q8;
+  const uint8_t* k8;
+  const uint8_t* v8;
+  const uint8_t* q_scale;  // [B][Hq][ceil(Sq/128)]
+  const uint8_t* k_scale;  // [B][Hkv][ceil(Skv/128)]
+  const uint8_t* v_scale;
+  void* o;                 // bf16 [B][Hq][Sq][D]
+  float* lse;
+  int B, Hq, Hkv, G, Sq, Skv, D;
+  int n_qt;
+  int window;
+  float scale_log2;
+};
+
 struct BwdArgs {
   const void* q;
   const void* k;

@@ -16,6 +16,10 @@ hipError_t launch_bwd_d(const BwdArgs& a, int mask, int mod, int phases, hipStre
 hipError_t launch_block_mask(int mask_kind, int window, const int32_t* doc_ids, int Sq, int Skv,
                              const BlockMaskArgs& m, hipStream_t st);
 
+hipError_t launch_fp8_fwd(const Fp8FwdArgs& a, int mask, hipStream_t st);
+hipError_t launch_fp8_quantize(const void* x, void* x8, uint8_t* scales, int rows, int S, int D, const float* signs,
+                               hipStream_t st);
+
 // Keys per forward step for each instantiation.
 constexpr int fwd_kv_step(bool f32) { return f32 ? 32 : 64; }
 
