@@ -24,6 +24,13 @@ Readings where the pages are silent (each one is listed in the design notes):
   * A row with no admissible key has output 0 and log-sum-exp -inf.
   * GQA maps query head h to key/value head h // (Hq // Hkv).
   * LSE is in natural-log units.
+  * The learnable bias (the FlexAttention/FA4 page lists gradients of
+    learnable bias tensors among FlexAttention's limits) is a per-query-head
+    table of the relative position i - j: the modifier adds
+    rel_bias[h][i - j + rel_origin] to the scaled score, with rel_origin =
+    Skv - 1 so the table [Hq][Sq + Skv - 1] covers every pair.  ALiBi is the
+    case of a linear table.  Its gradient is the sum of dS' (the gradient of
+    the modified score) over every (batch, i, j) that reads the entry.
 The backward pass is not on the pages; it is the chain rule of the same
 definition (see ``backward_head``).
 """
@@ -35,7 +42,7 @@ import math
 import numpy as np
 
 MASK_NONE, MASK_CAUSAL, MASK_SLIDING_WINDOW, MASK_DOCUMENT = 0, 1, 2, 3
-MOD_NONE, MOD_ALIBI, MOD_SOFTCAP, MOD_LOCAL_BOOST = 0, 1, 2, 3
+MOD_NONE, MOD_ALIBI, MOD_SOFTCAP, MOD_LOCAL_BOOST, MOD_REL_BIAS = 0, 1, 2, 3, 4
 TILE_EMPTY, TILE_PARTIAL, TILE_FULL = 0, 1, 2
 
 
@@ -50,6 +57,8 @@ class Variant:
     softcap: float = 0.0
     boost_radius: int = 0
     boost_factor: float = 1.0
+    rel_bias: np.ndarray | None = None     # [Hq][Sq + Skv - 1] (MOD_REL_BIAS)
+    rel_origin: int = 0                    # index of relative position 0: Skv - 1
 
 
 def default_alibi_slopes(Hq: int) -> np.ndarray:
@@ -89,12 +98,19 @@ def modify(var: Variant, s: np.ndarray, h: int, Hq: int, i: np.ndarray, j: np.nd
     if var.mod == MOD_LOCAL_BOOST:
         near = np.abs(I - J) < var.boost_radius
         return np.where(near, s * float(var.boost_factor), s)
+    if var.mod == MOD_REL_BIAS:
+        return s + np.asarray(var.rel_bias, dtype=np.float64)[h][rel_index(var, i, j)]
     raise ValueError(f"unknown score modifier {var.mod}")
+
+
+def rel_index(var: Variant, i, j) -> np.ndarray:
+    """Table index i - j + rel_origin of every pair, [len(i), len(j)]."""
+    return np.asarray(i, dtype=np.int64)[:, None] - np.asarray(j, dtype=np.int64)[None, :] + int(var.rel_origin)
 
 
 def modify_grad(var: Variant, s: np.ndarray, h: int, Hq: int, i: np.ndarray, j: np.ndarray) -> np.ndarray:
     """d modify / d s, elementwise."""
-    if var.mod in (MOD_NONE, MOD_ALIBI):
+    if var.mod in (MOD_NONE, MOD_ALIBI, MOD_REL_BIAS):
         return np.ones_like(s)
     if var.mod == MOD_SOFTCAP:
         t = np.tanh(s / float(var.softcap))
@@ -182,7 +198,7 @@ def probabilities(q_head, k_head, scale, var, b=0, h=0, Hq=1):
     return _softmax_rows(sm, ok)[0]
 
 
-def backward_head(q_h, k_h, v_h, do_h, scale, var, b, h, Hq, check_delta: bool = True):
+def backward_head(q_h, k_h, v_h, do_h, scale, var, b, h, Hq, check_delta: bool = True, with_dsp: bool = False):
     """Gradients of sum(O * dO) for one query head, by the chain rule.
 
     With s = scale q k^T, s' = mod(s), P = softmax over admissible keys and
@@ -190,7 +206,8 @@ def backward_head(q_h, k_h, v_h, do_h, scale, var, b, h, Hq, check_delta: bool =
     dS'_ij = P_ij (dP_ij - D_i),  dS = dS' * mod'(s),  dQ = scale dS K,
     dK = scale dS^T Q.  D_i is also formed as dO_i . O_i and the two must
     agree.  Returns (dq, dk, dv, O, LSE) for this head; dk and dv are this
-    query head's share of its key/value head's gradient.
+    query head's share of its key/value head's gradient.  ``with_dsp`` appends
+    dS' [Sq, Skv], the gradient of the modified scores (zero where masked).
     """
     q_h, k_h, v_h, do_h = _f64(q_h), _f64(k_h), _f64(v_h), _f64(do_h)
     Sq, Skv = q_h.shape[0], k_h.shape[0]
@@ -205,11 +222,14 @@ def backward_head(q_h, k_h, v_h, do_h, scale, var, b, h, Hq, check_delta: bool =
         Ddot = np.sum(do_h * O, axis=1)
         tol = 1e-9 * (1.0 + np.abs(Ddot).max(initial=0.0))
         assert np.allclose(Dsum, Ddot, rtol=1e-9, atol=tol), "D_i two ways disagree"
-    dS = P * (dP - Dsum[:, None]) * modify_grad(var, s, h, Hq, rows, cols)
+    dSp = P * (dP - Dsum[:, None])
+    dS = dSp * modify_grad(var, s, h, Hq, rows, cols)
     dQ = scale * (dS @ k_h)
     dK = scale * (dS.T @ q_h)
     with np.errstate(divide="ignore"):
         LSE = np.where(Z > 0, M + np.log(np.where(Z > 0, Z, 1.0)), -np.inf)
+    if with_dsp:
+        return dQ, dK, dV, O, LSE, dSp
     return dQ, dK, dV, O, LSE
 
 
@@ -234,6 +254,25 @@ def backward(q, k, v, do, scale: float, var: Variant | None = None, heads=None):
         dk[b, hk] += gk
         dv[b, hk] += gv
     return dq, dk, dv
+
+
+def rel_bias_grad(q, k, v, do, scale: float, var: Variant, heads=None) -> np.ndarray:
+    """Gradient of sum(O * dO) with respect to the MOD_REL_BIAS table
+    [Hq][Sq + Skv - 1].  The table entry r enters the modified score of
+    every pair (b, i, j) with i - j + rel_origin = r, with derivative 1, so
+    its gradient is the sum of dS'_bij over those pairs (np.add.at does the
+    scatter-sum).  ``heads``: optional list of (b, hq) to include."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, Hq, Sq, _ = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    G = np.zeros((Hq, Sq + Skv - 1))
+    rows, cols = np.arange(Sq), np.arange(Skv)
+    todo = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else list(heads)
+    for b, h in todo:
+        hk = kv_head(h, Hq, Hkv)
+        dSp = backward_head(q[b, h], k[b, hk], v[b, hk], do[b, h], scale, var, b, h, Hq, with_dsp=True)[5]
+        np.add.at(G[h], rel_index(var, rows, cols), dSp)
+    return G
 
 
 def loss(q, k, v, do, scale, var=None):

@@ -246,6 +246,7 @@ VARIANTS_FD = [
     dict(mask=0), dict(mask=1), dict(mask=2, window=3), dict(mask=3),
     dict(mask=1, mod=1), dict(mask=0, mod=2, softcap=1.5), dict(mask=1, mod=3, boost_radius=2, boost_factor=1.1),
     dict(mask=3, mod=2, softcap=2.0),
+    dict(mask=0, mod=4, rel_bias=np.random.default_rng(8).standard_normal((2, 13)), rel_origin=6),
 ]
 
 
@@ -326,10 +327,105 @@ def check_pair_counts(O):
     assert O.count_pairs(O.Variant(mask=O.MASK_DOCUMENT, doc_ids=doc), 1, S, S) == sum(L * (L + 1) // 2 for L in lens)
 
 
+def _rel_table(rng, Hq, Sq, Skv):
+    return rng.standard_normal((Hq, Sq + Skv - 1))
+
+
+def check_rel_bias_toeplitz(O):
+    """Q = 0 makes every scaled score 0, so the weight of key j in row i is
+    exp(T_h[i - j + Skv - 1]): a Toeplitz matrix, built here with
+    scipy.linalg.toeplitz from its first column (j = 0) and first row
+    (i = 0).  O = W V / rowsum(W), LSE = log rowsum(W); causal keeps the
+    lower triangle.  Pins the index direction and origin of the table."""
+    from scipy.linalg import toeplitz
+    rng = np.random.default_rng(21)
+    Hq, Sq, Skv, D = 2, 6, 9, 3
+    T = _rel_table(rng, Hq, Sq, Skv)
+    q = np.zeros((1, Hq, Sq, D))
+    k, v = rnd(1, 1, Skv, D, rng=rng), rnd(1, 1, Skv, D, rng=rng)
+    o = Skv - 1
+    for mask in (O.MASK_NONE, O.MASK_CAUSAL):
+        out, lse = O.forward(q, k, v, 0.7, O.Variant(mask=mask, mod=O.MOD_REL_BIAS, rel_bias=T, rel_origin=o))
+        for h in range(Hq):
+            W = np.exp(toeplitz(T[h, o:o + Sq], T[h, o - np.arange(Skv)]))
+            if mask == O.MASK_CAUSAL:
+                W = np.tril(W)
+            close(out[0, h], (W @ v[0, 0]) / W.sum(1)[:, None], 1e-12)
+            close(lse[0, h], np.log(W.sum(1)), 1e-12)
+
+
+def check_rel_bias_is_alibi(O):
+    """A table linear in the relative position, T_h[r] = slope_h (Skv - 1 - r)
+    = slope_h (j - i), gives the ALiBi modifier exactly, forward and
+    backward."""
+    rng = np.random.default_rng(22)
+    B, Hq, Hkv, Sq, Skv, D = 1, 4, 2, 7, 9, 3
+    slopes = O.default_alibi_slopes(Hq)
+    o = Skv - 1
+    T = slopes[:, None] * (o - np.arange(Sq + Skv - 1))[None, :]
+    q, k, v, do = rnd(B, Hq, Sq, D, rng=rng), rnd(B, Hkv, Skv, D, rng=rng), rnd(B, Hkv, Skv, D, rng=rng), rnd(B, Hq, Sq, D, rng=rng)
+    for mask in (O.MASK_NONE, O.MASK_CAUSAL):
+        a = O.Variant(mask=mask, mod=O.MOD_ALIBI)
+        r = O.Variant(mask=mask, mod=O.MOD_REL_BIAS, rel_bias=T, rel_origin=o)
+        for x, y in zip(O.forward(q, k, v, 0.4, a), O.forward(q, k, v, 0.4, r)):
+            close(y, x, 1e-12)
+        for x, y in zip(O.backward(q, k, v, do, 0.4, a), O.backward(q, k, v, do, 0.4, r)):
+            close(y, x, 1e-12)
+
+
+def check_rel_bias_shift(O):
+    """A constant table c_h shifts every admissible score of head h: O and
+    dQ, dK, dV are those without a modifier, LSE moves by c_h, and the table
+    gradient sums to zero over each head (every row of dS' sums to zero)."""
+    rng = np.random.default_rng(23)
+    B, Hq, S, D = 2, 2, 8, 4
+    c = np.array([0.75, -2.5])
+    T = np.repeat(c[:, None], 2 * S - 1, axis=1)
+    q, k, v, do = rnd(B, Hq, S, D, rng=rng), rnd(B, Hq, S, D, rng=rng), rnd(B, Hq, S, D, rng=rng), rnd(B, Hq, S, D, rng=rng)
+    for mask in (O.MASK_NONE, O.MASK_CAUSAL, O.MASK_SLIDING_WINDOW):
+        n = O.Variant(mask=mask, window=3)
+        r = O.Variant(mask=mask, window=3, mod=O.MOD_REL_BIAS, rel_bias=T, rel_origin=S - 1)
+        (o1, l1), (o2, l2) = O.forward(q, k, v, 0.5, n), O.forward(q, k, v, 0.5, r)
+        close(o2, o1, 1e-12)
+        close(l2, l1 + c[None, :, None], 1e-12)
+        for x, y in zip(O.backward(q, k, v, do, 0.5, n), O.backward(q, k, v, do, 0.5, r)):
+            close(y, x, 1e-12)
+        g = O.rel_bias_grad(q, k, v, do, 0.5, r)
+        assert g.shape == (Hq, 2 * S - 1)
+        close(g.sum(1), np.zeros(Hq), 1e-12)
+        assert np.abs(g).max() > 1e-3
+
+
+def check_rel_bias_grad_fd(O, h=1e-6, tol=1e-6):
+    """Central differences of sum(O * dO) with respect to every table entry,
+    under each mask, with GQA, two batch rows and Sq != Skv."""
+    rng = np.random.default_rng(24)
+    B, Hq, Hkv, D = 2, 4, 2, 3
+    doc = np.array([[0, 0, 1, 1, 1, 2, 2], [0, 1, 1, 1, 1, 1, 2]], dtype=np.int32)
+    for mask, Sq, Skv in ((O.MASK_NONE, 5, 7), (O.MASK_CAUSAL, 7, 7), (O.MASK_SLIDING_WINDOW, 7, 7),
+                          (O.MASK_DOCUMENT, 7, 7)):
+        T = _rel_table(rng, Hq, Sq, Skv)
+        var = O.Variant(mask=mask, window=3, doc_ids=doc, mod=O.MOD_REL_BIAS, rel_bias=T, rel_origin=Skv - 1)
+        q, k, v, do = rnd(B, Hq, Sq, D, rng=rng), rnd(B, Hkv, Skv, D, rng=rng), rnd(B, Hkv, Skv, D, rng=rng), rnd(B, Hq, Sq, D, rng=rng)
+        g = O.rel_bias_grad(q, k, v, do, 0.6, var)
+        num = np.zeros_like(T)
+        for idx in np.ndindex(T.shape):
+            old = T[idx]
+            T[idx] = old + h
+            lp = O.loss(q, k, v, do, 0.6, var)
+            T[idx] = old - h
+            lm = O.loss(q, k, v, do, 0.6, var)
+            T[idx] = old
+            num[idx] = (lp - lm) / (2 * h)
+        err = np.max(np.abs(num - g)) / (1.0 + np.max(np.abs(g)))
+        assert err <= tol, f"mask {mask}: table gradient mismatch {err:.2e}"
+
+
 ALL_CHECKS = [
     check_identical_keys, check_single_token, check_causal_row0, check_window_edges,
     check_document_concat, check_alibi_geometric, check_alibi_zero_slope,
     check_softcap_closed_form, check_softcap_limits, check_local_boost_two_level,
     check_invariants, check_gqa_equals_repeat, check_backward_closed_forms,
     check_tile_states, check_pair_counts,
+    check_rel_bias_toeplitz, check_rel_bias_is_alibi, check_rel_bias_shift, check_rel_bias_grad_fd,
 ]

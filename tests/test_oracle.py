@@ -100,8 +100,46 @@ def _bad_kv_head(h, Hq, Hkv):
     return h % Hkv
 
 
+def _bad_rel_direction(var, s, h, Hq, i, j):
+    if var.mod == oracle.MOD_REL_BIAS:
+        T = np.asarray(var.rel_bias)
+        idx = (np.asarray(j)[None, :] - np.asarray(i)[:, None] + var.rel_origin) % T.shape[1]
+        return s + T[h][idx]
+    return _orig_modify(var, s, h, Hq, i, j)
+
+
+def _bad_rel_origin(var, s, h, Hq, i, j):
+    if var.mod == oracle.MOD_REL_BIAS:
+        T = np.asarray(var.rel_bias)
+        return s + T[h][(OA.rel_index(var, i, j) + 1) % T.shape[1]]
+    return _orig_modify(var, s, h, Hq, i, j)
+
+
+def _bad_rel_grad_transposed(q, k, v, do, scale, var, heads=None):
+    """Scatters dS'_ij to entry j - i + origin instead of i - j + origin."""
+    g = _orig_rel_bias_grad(q, k, v, do, scale, var, heads)
+    return g[:, ::-1].copy()
+
+
+def _bad_rel_grad_no_delta(q, k, v, do, scale, var, heads=None):
+    """Forms the table gradient from P dP, dropping the - D_i term."""
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    B, Hq, Sq, _ = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    G = np.zeros((Hq, Sq + Skv - 1))
+    rows, cols = np.arange(Sq), np.arange(Skv)
+    for b in range(B):
+        for h in range(Hq):
+            hk = OA.kv_head(h, Hq, Hkv)
+            _, sm, ok = OA.score_rows(q[b, h], k[b, hk], scale, var, b, h, Hq, rows, Skv)
+            P = OA._softmax_rows(sm, ok)[0]
+            np.add.at(G[h], OA.rel_index(var, rows, cols), P * (do[b, h] @ v[b, hk].T))
+    return G
+
+
 _orig_allowed = OA.allowed
 _orig_modify = OA.modify
+_orig_rel_bias_grad = OA.rel_bias_grad
 
 MUTATIONS = {
     "window_le": ("allowed", _bad_window_le),
@@ -111,6 +149,10 @@ MUTATIONS = {
     "boost_le": ("modify", _bad_boost_le),
     "softcap_grad_dropped": ("modify_grad", _bad_softcap_grad),
     "gqa_interleaved_heads": ("kv_head", _bad_kv_head),
+    "rel_bias_direction": ("modify", _bad_rel_direction),
+    "rel_bias_origin": ("modify", _bad_rel_origin),
+    "rel_bias_grad_transposed": ("rel_bias_grad", _bad_rel_grad_transposed),
+    "rel_bias_grad_no_delta": ("rel_bias_grad", _bad_rel_grad_no_delta),
 }
 
 
