@@ -27,8 +27,8 @@
  *  - Ownership: the caller owns every buffer.  The library allocates no
  *    device memory, keeps no mutable global state, and is re-entrant.
  *    Parameter structs are host memory read during the call only; the
- *    arrays they point to (doc_ids, alibi_slopes, block-mask arrays) are
- *    device memory.
+ *    arrays they point to (doc_ids, alibi_slopes, rel_bias and its gradient
+ *    and scratch, block-mask arrays) are device memory.
  *  - Errors: an fa_status is returned.  All argument validation happens
  *    before any HIP call, so an invalid call has no device side effect.
  *    A failed launch maps to FA_ERR_LAUNCH.  Nothing is thrown or aborted.
@@ -77,7 +77,11 @@ typedef enum {
   FA_MOD_NONE = 0,
   FA_MOD_ALIBI = 1,       /* s + slope[h] * (j - i) */
   FA_MOD_SOFTCAP = 2,     /* softcap * tanh(s / softcap) */
-  FA_MOD_LOCAL_BOOST = 3  /* |i - j| < boost_radius ? s * boost_factor : s */
+  FA_MOD_LOCAL_BOOST = 3, /* |i - j| < boost_radius ? s * boost_factor : s */
+  FA_MOD_REL_BIAS = 4     /* s + rel_bias[h][i - j + Skv - 1]: a learnable
+                             relative-position bias (the same page lists the
+                             gradients of learnable bias tensors among
+                             FlexAttention's limits; fa_bwd returns it) */
 } fa_mod_kind;
 
 typedef struct {
@@ -94,6 +98,18 @@ typedef struct {
   float softcap;             /* FA_MOD_SOFTCAP: > 0 */
   int32_t boost_radius;      /* FA_MOD_LOCAL_BOOST: >= 0 */
   float boost_factor;        /* FA_MOD_LOCAL_BOOST: finite */
+  const float* rel_bias;     /* FA_MOD_REL_BIAS: device float [Hq][Sq + Skv - 1],
+                                entry i - j + Skv - 1 is added to the scaled
+                                score of (query i, key j) of query head h */
+  float* rel_bias_grad;      /* fa_bwd / fa_bwd_phase with FA_MOD_REL_BIAS (DQ
+                                phase): NULL, or device float [Hq][Sq + Skv - 1]
+                                that is overwritten with d(sum O * dout) /
+                                d rel_bias, summed over the batch in a fixed
+                                order (deterministic) */
+  float* rel_bias_ws;        /* required with rel_bias_grad: device scratch of
+                                at least rel_bias_ws_bytes bytes, 16-byte
+                                aligned, contents need not be initialised */
+  size_t rel_bias_ws_bytes;  /* >= fa_bwd_rel_bias_workspace_bytes(B, Hq, Sq, Skv) */
 } fa_mod_params;
 
 /* Tile states of a block mask. */
@@ -150,8 +166,10 @@ int fa_fwd_kv_step(int D, int dtype);
  * float32 and rounding once.  workspace: device, at least
  * fa_bwd_workspace_bytes(B, Hq, Sq, D) bytes, 16-byte aligned, contents
  * need not be initialised (it receives two [B][Hq][Sq] float arrays: the
- * row sums of dout * out and the LSE in log2 units).  Supported: dtype FA_BF16, D in {64, 128}, every
- * mask and modifier. */
+ * row sums of dout * out and the LSE in log2 units).  Supported: dtype
+ * FA_BF16, D in {64, 128}, every mask and modifier.  With FA_MOD_REL_BIAS
+ * and mod_params->rel_bias_grad set, the DQ phase also writes the bias
+ * table's gradient (see fa_mod_params). */
 int fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
            int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype, float scale,
@@ -174,6 +192,12 @@ int fa_bwd_phase(int phase, const void* q, const void* k, const void* v, const v
                  const fa_block_mask* block_mask, void* stream);
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq, int D);
+
+/* Size of the scratch a relative-bias gradient needs (fa_mod_params
+ * rel_bias_ws): one float row of Skv + 128 per (batch, query head, 128-row
+ * query tile), the per-tile diagonal sums that a fixed-order reduction then
+ * adds up.  0 when any size is 0. */
+size_t fa_bwd_rel_bias_workspace_bytes(int B, int Hq, int Sq, int Skv);
 
 /* FP8 path ("FlashAttention-3 (KO)" page, technical innovation 3: FP8
  * doubles the matrix throughput of 16-bit formats; incoherent processing

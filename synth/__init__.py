@@ -42,6 +42,15 @@ def qkv(B, Hq, Hkv, Sq, Skv, D, seed: int, dtype: str = "bf16"):
     return q, k, v
 
 
+def rel_bias_table(Hq: int, Sq: int, Skv: int, seed: int, std: float = 1.0) -> torch.Tensor:
+    """A relative-position bias table [Hq, Sq + Skv - 1]: float32 N(0, std^2)
+    from a seeded CPU generator (entry i - j + Skv - 1 belongs to query i and
+    key j)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return (torch.randn(Hq, max(Sq + Skv - 1, 0), generator=g, dtype=torch.float32) * std).contiguous()
+
+
 def doc_lengths(total: int, lo: int, hi: int, seed: int) -> np.ndarray:
     """Packed document lengths: uniform integers in [lo, hi], last one truncated."""
     rng = np.random.default_rng(seed)

@@ -46,7 +46,12 @@ def bf16_half_ulp(x):
     return np.where(a >= 2.0 ** -126, 2.0 ** (e - 8), 2.0 ** -134)
 
 
-def check_out(got, ref, dtype: str, what: str = "O", max_excess=None):
+def check_out(got, ref, dtype: str, what: str = "O", max_excess=None, rounding_mean=False):
+    """``rounding_mean``: hold the mean, like the max, to the error beyond
+    half a bf16 ulp.  Only for outputs whose magnitude alone puts the mean
+    rounding error over the mean bar (e.g. dV of a single key, the sum of
+    every dO row: |dV| ~ 11 at 130 rows, where the mean rounding error of
+    any bf16 value is ~1e-2)."""
     mx, mean = err_stats(got, ref)
     bmax, bmean = BARS[dtype]
     if max_excess is not None:
@@ -55,7 +60,10 @@ def check_out(got, ref, dtype: str, what: str = "O", max_excess=None):
     if dtype == "bf16":
         g = got.detach().to("cpu", torch.float64).numpy()
         r = np.asarray(ref, dtype=np.float64)
-        excess = float(np.max(np.abs(g - r) - bf16_half_ulp(r), initial=0.0))
+        beyond = np.maximum(np.abs(g - r) - bf16_half_ulp(r), 0.0)
+        excess = float(np.max(beyond, initial=0.0))
+        if rounding_mean:
+            mean = float(beyond.mean()) if beyond.size else 0.0
     assert excess <= bmax and mean <= bmean, (
         f"{what}: max {mx:.3e} (beyond bf16 rounding {excess:.3e}, bar {bmax}), mean {mean:.3e} (bar {bmean})")
     return mx, mean

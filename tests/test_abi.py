@@ -177,3 +177,31 @@ def test_fp8_quantize_validation():
     assert L.fa_fp8_quantize(MIS, P, P, 2, 16, 64, None, None) == fa.FA_ERR_ALIGN
     assert L.fa_fp8_quantize(P, P, P, 2, 16, 64, ctypes.c_void_p(0x100002), None) == fa.FA_ERR_ALIGN
     assert L.fa_fp8_quantize(None, None, None, 0, 16, 64, None, None) == fa.FA_OK
+
+
+def test_rel_bias_validation():
+    """Relative-bias modifier: table required and aligned; its gradient needs
+    an aligned output and enough scratch (fa_bwd_rel_bias_workspace_bytes)."""
+    assert fa.fa_bwd_rel_bias_workspace_bytes(2, 16, 8192, 8192) == 2 * 16 * 64 * (8192 + 128) * 4
+    assert fa.fa_bwd_rel_bias_workspace_bytes(1, 2, 300, 100) == 1 * 2 * 3 * (100 + 128) * 4
+    assert fa.fa_bwd_rel_bias_workspace_bytes(0, 2, 300, 100) == 0
+    assert fa.fa_bwd_rel_bias_workspace_bytes(1, 2, 0, 100) == 0
+    table = 0x500000
+    assert fwd(mod=4) == fa.FA_ERR_NULL
+    assert fwd(mod=4, op=fa.FaModParams(None, 0.0, 0, 1.0, None)) == fa.FA_ERR_NULL
+    assert fwd(mod=4, op=fa.FaModParams(None, 0.0, 0, 1.0, 0x500002)) == fa.FA_ERR_ALIGN
+    need = fa.fa_bwd_rel_bias_workspace_bytes(1, 2, 16, 16)
+
+    def bwd_rel(grad, ws, ws_bytes, phase=7):
+        op = fa.FaModParams(None, 0.0, 0, 1.0, table, grad, ws, ws_bytes)
+        return fa.fa_bwd_phase(phase, P, P, P, P, P, P, P, P, P, P, 1 << 20, 1, 2, 2, 16, 16, 64, 0, 0.125,
+                               0, None, 4, ctypes.byref(op), None, None)
+
+    assert bwd_rel(0x600000, None, 0) == fa.FA_ERR_WORKSPACE
+    assert bwd_rel(0x600000, 0x700000, need - 4) == fa.FA_ERR_WORKSPACE
+    assert bwd_rel(0x600002, 0x700000, need) == fa.FA_ERR_ALIGN
+    assert bwd_rel(0x600000, 0x700008, need) == fa.FA_ERR_ALIGN
+    # other validation still comes first
+    op = fa.FaModParams(None, 0.0, 0, 1.0, None, 0x600000, 0x700000, need)
+    assert fa.fa_bwd(P, P, P, P, P, P, P, P, P, P, 1 << 20, 1, 2, 2, 16, 16, 64, 0, 0.125, 0, None, 4,
+                     ctypes.byref(op), None, None) == fa.FA_ERR_NULL

@@ -20,13 +20,14 @@ FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED = 0, -1, -2, -3
 FA_ERR_ALIGN, FA_ERR_PARAM, FA_ERR_WORKSPACE, FA_ERR_LAUNCH = -4, -5, -6, -7
 FA_BF16, FA_F32 = 0, 1
 MASK_NONE, MASK_CAUSAL, MASK_SLIDING_WINDOW, MASK_DOCUMENT = 0, 1, 2, 3
-MOD_NONE, MOD_ALIBI, MOD_SOFTCAP, MOD_LOCAL_BOOST = 0, 1, 2, 3
+MOD_NONE, MOD_ALIBI, MOD_SOFTCAP, MOD_LOCAL_BOOST, MOD_REL_BIAS = 0, 1, 2, 3, 4
 TILE_EMPTY, TILE_PARTIAL, TILE_FULL = 0, 1, 2
 BLOCK = 128
 
 FA_BWD_DELTA, FA_BWD_DKDV, FA_BWD_DQ = 1, 2, 4
 
 EXPORTED = ("fa_fwd", "fa_fwd_kv_step", "fa_bwd", "fa_bwd_phase", "fa_bwd_workspace_bytes",
+            "fa_bwd_rel_bias_workspace_bytes",
             "fa_block_mask_build", "fa_fp8_quantize", "fa_fwd_fp8", "fa_status_str", "fa_version")
 
 
@@ -36,7 +37,9 @@ class FaMaskParams(ctypes.Structure):
 
 class FaModParams(ctypes.Structure):
     _fields_ = [("alibi_slopes", ctypes.c_void_p), ("softcap", ctypes.c_float),
-                ("boost_radius", ctypes.c_int32), ("boost_factor", ctypes.c_float)]
+                ("boost_radius", ctypes.c_int32), ("boost_factor", ctypes.c_float),
+                ("rel_bias", ctypes.c_void_p), ("rel_bias_grad", ctypes.c_void_p),
+                ("rel_bias_ws", ctypes.c_void_p), ("rel_bias_ws_bytes", ctypes.c_size_t)]
 
 
 class FaBlockMask(ctypes.Structure):
@@ -79,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_phase.restype = _I
         L.fa_bwd_workspace_bytes.argtypes = [_I, _I, _I, _I]
         L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.fa_bwd_rel_bias_workspace_bytes.argtypes = [_I, _I, _I, _I]
+        L.fa_bwd_rel_bias_workspace_bytes.restype = ctypes.c_size_t
         L.fa_block_mask_build.argtypes = [_I, ctypes.POINTER(FaMaskParams), _I, _I, _I,
                                           ctypes.POINTER(FaBlockMask), _P]
         L.fa_block_mask_build.restype = _I
@@ -117,6 +122,10 @@ def fa_block_mask_build(*args) -> int:
 
 def fa_bwd_workspace_bytes(B: int, Hq: int, Sq: int, D: int) -> int:
     return int(lib().fa_bwd_workspace_bytes(B, Hq, Sq, D))
+
+
+def fa_bwd_rel_bias_workspace_bytes(B: int, Hq: int, Sq: int, Skv: int) -> int:
+    return int(lib().fa_bwd_rel_bias_workspace_bytes(B, Hq, Sq, Skv))
 
 
 def fa_fwd_kv_step(D: int, dtype: int) -> int:
@@ -162,11 +171,13 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _params(mask, window, doc_ids, visited, mod, alibi_slopes, softcap, boost_radius, boost_factor):
-    mp = FaMaskParams(int(window), None if doc_ids is None else doc_ids.data_ptr(),
-                      None if visited is None else visited.data_ptr())
-    op = FaModParams(None if alibi_slopes is None else alibi_slopes.data_ptr(), float(softcap),
-                     int(boost_radius), float(boost_factor))
+def _params(mask, window, doc_ids, visited, mod, alibi_slopes, softcap, boost_radius, boost_factor,
+            rel_bias=None, rel_bias_grad=None, rel_bias_ws=None):
+    ptr = lambda t: None if t is None else t.data_ptr()
+    mp = FaMaskParams(int(window), ptr(doc_ids), ptr(visited))
+    ws_bytes = 0 if rel_bias_ws is None else rel_bias_ws.numel() * rel_bias_ws.element_size()
+    op = FaModParams(ptr(alibi_slopes), float(softcap), int(boost_radius), float(boost_factor),
+                     ptr(rel_bias), ptr(rel_bias_grad), ptr(rel_bias_ws), int(ws_bytes))
     return mp, op
 
 
@@ -249,9 +260,11 @@ def build_block_mask(mask: int, B: int, Sq: int, Skv: int, *, window: int = 0, d
 
 
 def forward(q, k, v, *, scale=None, mask=MASK_NONE, window=0, doc_ids=None, mod=MOD_NONE,
-            alibi_slopes=None, softcap=0.0, boost_radius=0, boost_factor=1.0, block_mask=None,
-            return_lse=False, out=None, lse=None, visited=None, stream=None):
-    """O (and LSE if ``return_lse``) for q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] on the GPU."""
+            alibi_slopes=None, softcap=0.0, boost_radius=0, boost_factor=1.0, rel_bias=None,
+            block_mask=None, return_lse=False, out=None, lse=None, visited=None, stream=None):
+    """O (and LSE if ``return_lse``) for q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] on the GPU.
+
+    ``rel_bias`` (MOD_REL_BIAS): float32 [Hq, Sq + Skv - 1] on the device."""
     torch = _torch()
     B, Hq, Sq, D = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
@@ -259,7 +272,8 @@ def forward(q, k, v, *, scale=None, mask=MASK_NONE, window=0, doc_ids=None, mod=
         out = torch.empty_like(q)
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    mp, op = _params(mask, window, doc_ids, visited, mod, alibi_slopes, softcap, boost_radius, boost_factor)
+    mp, op = _params(mask, window, doc_ids, visited, mod, alibi_slopes, softcap, boost_radius, boost_factor,
+                     rel_bias)
     bms = block_mask.struct() if block_mask is not None else None
     rc = fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse) if return_lse else None,
                 B, Hq, Hkv, Sq, Skv, D, _dtype_code(q), float(default_scale(D) if scale is None else scale),
@@ -272,12 +286,16 @@ def forward(q, k, v, *, scale=None, mask=MASK_NONE, window=0, doc_ids=None, mod=
 
 def backward(q, k, v, out, dout, lse, *, scale=None, mask=MASK_NONE, window=0, doc_ids=None,
              mod=MOD_NONE, alibi_slopes=None, softcap=0.0, boost_radius=0, boost_factor=1.0,
+             rel_bias=None, rel_bias_grad=None, rel_bias_ws=None,
              block_mask=None, workspace=None, grads=None, stream=None,
              phases=FA_BWD_DELTA | FA_BWD_DKDV | FA_BWD_DQ):
     """(dq, dk, dv) of sum(O * dout), recomputing P from ``lse``.
 
     ``phases`` selects which of the three backward launches run (all by
-    default, which is fa_bwd)."""
+    default, which is fa_bwd).  With MOD_REL_BIAS, ``rel_bias_grad`` (float32
+    [Hq, Sq + Skv - 1], or True to allocate it) receives the gradient of the
+    bias table; its scratch ``rel_bias_ws`` is allocated when not given.  The
+    return value is then (dq, dk, dv, rel_bias_grad)."""
     torch = _torch()
     B, Hq, Sq, D = q.shape
     Hkv, Skv = k.shape[1], k.shape[2]
@@ -285,7 +303,14 @@ def backward(q, k, v, out, dout, lse, *, scale=None, mask=MASK_NONE, window=0, d
     ws_bytes = fa_bwd_workspace_bytes(B, Hq, Sq, D)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    mp, op = _params(mask, window, doc_ids, None, mod, alibi_slopes, softcap, boost_radius, boost_factor)
+    want_bias_grad = rel_bias_grad is not None
+    if rel_bias_grad is True:
+        rel_bias_grad = torch.empty((Hq, Sq + Skv - 1), dtype=torch.float32, device=q.device)
+    if want_bias_grad and rel_bias_ws is None:
+        rel_bias_ws = torch.empty(max(fa_bwd_rel_bias_workspace_bytes(B, Hq, Sq, Skv), 16), dtype=torch.uint8,
+                                  device=q.device)
+    mp, op = _params(mask, window, doc_ids, None, mod, alibi_slopes, softcap, boost_radius, boost_factor,
+                     rel_bias, rel_bias_grad, rel_bias_ws)
     bms = block_mask.struct() if block_mask is not None else None
     rc = fa_bwd_phase(int(phases), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                 _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -294,4 +319,6 @@ def backward(q, k, v, out, dout, lse, *, scale=None, mask=MASK_NONE, window=0, d
                 ctypes.byref(bms) if bms is not None else None, _stream(stream))
     if rc != FA_OK:
         raise FaError(rc, "fa_bwd_phase")
+    if want_bias_grad:
+        return dq, dk, dv, rel_bias_grad
     return dq, dk, dv

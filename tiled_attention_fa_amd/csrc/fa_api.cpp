@@ -35,7 +35,7 @@ int check_variant(int B, int Hq, int Sq, int Skv, float scale, int mask_kind, co
                   int mod_kind, const fa_mod_params* op, MaskArgs& mask, ModArgs& mod) {
   if (!std::isfinite(scale) || scale < 0.0f) return FA_ERR_PARAM;
   mask = MaskArgs{0, nullptr};
-  mod = ModArgs{nullptr, 1.0f, 1.0f, 0, 1.0f};
+  mod = ModArgs{nullptr, 1.0f, 1.0f, 0, 1.0f, nullptr, nullptr, nullptr};
   switch (mask_kind) {
     case FA_MASK_NONE:
     case FA_MASK_CAUSAL: break;
@@ -71,6 +71,11 @@ int check_variant(int B, int Hq, int Sq, int Skv, float scale, int mask_kind, co
       if (op->boost_radius < 0 || !std::isfinite(op->boost_factor)) return FA_ERR_PARAM;
       mod.boost_radius = op->boost_radius;
       mod.boost_factor = op->boost_factor;
+      break;
+    case FA_MOD_REL_BIAS:
+      if (!op || !op->rel_bias) return FA_ERR_NULL;
+      if (!aligned(op->rel_bias, 4)) return FA_ERR_ALIGN;
+      mod.rel_bias = op->rel_bias;
       break;
     default: return FA_ERR_UNSUPPORTED;
   }
@@ -242,6 +247,11 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq, int D) {
   return 2 * ws_half(B, Hq, Sq);
 }
 
+size_t fa_bwd_rel_bias_workspace_bytes(int B, int Hq, int Sq, int Skv) {
+  if (B <= 0 || Hq <= 0 || Sq <= 0 || Skv < 0) return 0;
+  return (size_t)B * Hq * (size_t)cdiv(Sq, kTileQ) * ((size_t)Skv + kBiasRowPad) * sizeof(float);
+}
+
 int fa_bwd_phase(int phase, const void* q, const void* k, const void* v, const void* out, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes, int B, int Hq,
                  int Hkv, int Sq, int Skv, int D, int dtype, float scale, int mask_kind,
@@ -267,7 +277,21 @@ int fa_bwd_phase(int phase, const void* q, const void* k, const void* v, const v
     if (!workspace || ws_bytes < fa_bwd_workspace_bytes(B, Hq, Sq, D)) return FA_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
   }
-  if (B == 0) return FA_OK;
+  // Relative-bias gradient: output table and the per-tile scratch.
+  const bool bias_grad = score_mod_kind == FA_MOD_REL_BIAS && mod_params->rel_bias_grad != nullptr &&
+                         (phase & FA_BWD_DQ) && (long long)Sq + Skv > 1;
+  if (bias_grad) {
+    if (!aligned(mod_params->rel_bias_grad, 4)) return FA_ERR_ALIGN;
+    if ((long long)Hq * cdiv((long long)Sq + Skv - 1, 256) > kMaxGrid) return FA_ERR_SHAPE;
+    const size_t need = fa_bwd_rel_bias_workspace_bytes(B, Hq, Sq, Skv);
+    if (need > 0) {
+      if (!mod_params->rel_bias_ws || mod_params->rel_bias_ws_bytes < need) return FA_ERR_WORKSPACE;
+      if (!aligned(mod_params->rel_bias_ws, 16)) return FA_ERR_ALIGN;
+      a.mod.rel_bias_part = mod_params->rel_bias_ws;
+    }
+    a.mod.rel_bias_grad = mod_params->rel_bias_grad;
+  }
+  if (B == 0 && !bias_grad) return FA_OK;
 
   a.q = q;
   a.k = k;

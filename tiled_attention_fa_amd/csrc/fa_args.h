@@ -5,7 +5,7 @@
 namespace miattn {
 
 enum { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_WINDOW = 2, MASK_DOCUMENT = 3 };
-enum { MOD_NONE = 0, MOD_ALIBI = 1, MOD_SOFTCAP = 2, MOD_BOOST = 3 };
+enum { MOD_NONE = 0, MOD_ALIBI = 1, MOD_SOFTCAP = 2, MOD_BOOST = 3, MOD_REL_BIAS = 4 };
 enum { TILE_EMPTY = 0, TILE_PARTIAL = 1, TILE_FULL = 2 };
 
 // Query rows per workgroup and the block-mask granularity; the forward,
@@ -23,7 +23,18 @@ struct ModArgs {
   float softcap, inv_softcap;
   int boost_radius;
   float boost_factor;
+  // Relative-position bias: s + rel_bias[h][i - j + Skv - 1], [Hq][Sq + Skv - 1].
+  const float* rel_bias;
+  // Backward only, may be null: per-(batch, head, query tile) partial sums of
+  // the table gradient ([B][Hq][n_qt][Skv + kBiasRowPad], written by the dQ
+  // kernel) and the gradient itself ([Hq][Sq + Skv - 1], their sum).
+  float* rel_bias_part;
+  float* rel_bias_grad;
 };
+
+// A dQ workgroup's partial row covers the diagonals i - j of its 128 query
+// rows: [q0 - Skv + 1, q0 + 127], Skv + 127 entries, padded to Skv + 128.
+constexpr int kBiasRowPad = 128;
 
 struct BlockMaskArgs {
   uint8_t* tile_state;  // null: tile ranges follow from the mask kind

@@ -48,14 +48,18 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 }
 
 // Probability, and the factor that turns dP - delta into dS, for one
-// (query i, key j) score: x2 is the modified score in log2 units.
+// (query i, key j) score: x2 is the modified score in log2 units.  `bias` is
+// the relative-bias table entry of the pair (MOD_REL_BIAS only).
 template <int MOD>
-__device__ __forceinline__ void recompute_p(float sraw, int i, int j, float slope, const BwdArgs& a,
+__device__ __forceinline__ void recompute_p(float sraw, int i, int j, float slope, float bias, const BwdArgs& a,
                                             float lse2, float& p, float& grad) {
   float x2;
   grad = 1.0f;
   if constexpr (MOD == MOD_NONE) {
     x2 = sraw * a.scale_log2;
+  } else if constexpr (MOD == MOD_REL_BIAS) {
+    p = fast_exp2(__builtin_fmaf(__builtin_fmaf(sraw, a.scale, bias), kLog2e, -lse2));
+    return;
   } else if constexpr (MOD == MOD_ALIBI) {
     x2 = (sraw * a.scale + slope * (float)(j - i)) * kLog2e;
   } else if constexpr (MOD == MOD_SOFTCAP) {
@@ -94,6 +98,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // 64 entries each: one per lane of the loading wave (the last 32 are unused).
   __shared__ __attribute__((aligned(16))) float sL0[64], sE0[64], sL1[64], sE1[64];
   __shared__ __attribute__((aligned(16))) int sD0[64], sD1[64];
+  // Relative-bias diagonals of one step: BQ + BK - 1 = 159 entries, 3 chunks of 64.
+  constexpr bool REL = MOD == MOD_REL_BIAS;
+  __shared__ __attribute__((aligned(16))) float sB0[REL ? 192 : 1], sB1[REL ? 192 : 1];
 
   int b, hk, kt;
   decode_work(blockIdx.x, a.B, a.Hkv, a.Hkv, a.n_kt, false, b, hk, kt);
@@ -161,7 +168,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return blk * BQ;
   };
 
-  auto issue = [&](Pos p, int blk, char* qn, char* on, float* ln, float* en, int* dn) {
+  const int tlen = Sq + Skv - 1;
+  auto issue = [&](Pos p, int blk, char* qn, char* on, float* ln, float* en, int* dn, float* bn) {
     const int hq = hk * G + p.g, q0 = query0(p, blk);
     const size_t head = (size_t)(b * a.Hq + hq) * Sq;
     tile_load<D, BQ>(rows_rsrc((const uint16_t*)a.q + head * D, Sq, q0, ROW), qn, wave, lane);
@@ -170,6 +178,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (wave == 1) ints_to_lds(a.delta + head, Sq, q0, (int*)en, lane);
     if constexpr (MASK == MASK_DOCUMENT) {
       if (wave == 2) ints_to_lds(doc, Skv, q0, dn, lane);
+    }
+    if constexpr (REL) {
+      // Entry e: i - j = q0 - k0 - (BK - 1) + e.
+      if (wave < 3)
+        bias_chunk_to_lds(uniform_ptr(a.mod.rel_bias + (size_t)hq * tlen), tlen, q0 - k0 - (BK - 1) + (Skv - 1), bn,
+                          wave, lane);
     }
   };
 
@@ -185,9 +199,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   Pos pn = advance(pc);
   Pos pnn = advance(pn);
   auto step = [&](int s, const char* qs, const char* ds, const float* ls, const float* es, const int* dcs,
-                  char* qn, char* on, float* ln, float* en, int* dn) {
+                  const float* bs, char* qn, char* on, float* ln, float* en, int* dn, float* bn) {
     const bool have_next = s + 1 < n_steps;
-    if (have_next) issue(pn, blk_n, qn, on, ln, en, dn);
+    if (have_next) issue(pn, blk_n, qn, on, ln, en, dn, bn);
     const int blk_nn = fetch_blk(s + 2, pnn);
     if constexpr (BM) st_n = have_next ? bm_state[(size_t)blk_n * a.bm.n_kv] : 0;
     const int hq = hk * G + pc.g;
@@ -213,7 +227,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                        *(const u32x4*)(sV + vrow * ROW + swz<D>(vrow, 2 * c + hh) * 16), dp);
       }
       // P and dS (register r: query q0 + 8(r/4) + 4hh + r%4).  Full tiles
-      // take a branch without the mask test.
+      // take a branch without the mask test.  bl[8 rq + e] is the bias of
+      // query q0 + 8 rq + 4hh + e and this lane's key.
+      const float* bl = bs + (BK - 1 - 32 * wave - l32 + 4 * hh);
       auto pds = [&](auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
@@ -225,7 +241,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int e = 0; e < 4; ++e) {
             const int i = q0 + ir + e;
             float p, grad;
-            recompute_p<MOD>(sp[4 * rq + e], i, kj, slope, a, L4[e], p, grad);
+            recompute_p<MOD>(sp[4 * rq + e], i, kj, slope, REL ? bl[8 * rq + e] : 0.0f, a, L4[e], p, grad);
             if constexpr (MASKED) {
               int di = 0;
               if constexpr (MASK == MASK_DOCUMENT) di = dcs[ir + e];
@@ -272,13 +288,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if constexpr (BM) st_c = n_steps > 0 ? bm_state[(size_t)blk_c * a.bm.n_kv] : 0;
   if (n_steps > 0) {
     tile_load<D, BK>(rows_rsrc(Vh, Skv, k0, ROW), sV, wave, lane);
-    issue(pc, blk_c, sQ0, sO0, sL0, sE0, sD0);
+    issue(pc, blk_c, sQ0, sO0, sL0, sE0, sD0, sB0);
     wait_loads();
   }
   __syncthreads();
   for (int s = 0; s < n_steps; s += 2) {
-    step(s, sQ0, sO0, sL0, sE0, sD0, sQ1, sO1, sL1, sE1, sD1);
-    if (s + 1 < n_steps) step(s + 1, sQ1, sO1, sL1, sE1, sD1, sQ0, sO0, sL0, sE0, sD0);
+    step(s, sQ0, sO0, sL0, sE0, sD0, sB0, sQ1, sO1, sL1, sE1, sD1, sB1);
+    if (s + 1 < n_steps) step(s + 1, sQ1, sO1, sL1, sE1, sD1, sB1, sQ0, sO0, sL0, sE0, sD0, sB0);
   }
 
   if (col_ok) {
@@ -302,6 +318,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // column per lane, as in the forward kernel).  Per step: 64 keys, K and V
 // tiles in LDS.  S^T = K Q^T and dP^T = V dO^T give dS^T with a query per
 // lane; dQ^T += K^T dS^T takes K^T from transposing LDS reads.
+//
+// Relative-bias gradient (rel_bias_part set): the gradient of table entry
+// i - j + Skv - 1 sums dS' over that diagonal.  Each step adds its dS'
+// values into per-(wave, half-wave) LDS slices indexed by diagonal, with no
+// two lanes of one instruction on the same entry, so the sums are
+// deterministic.  At the start of the next step the slices are summed in a
+// fixed order into a 256-entry ring indexed by the diagonal mod 256.  Keys
+// only grow from step to step, so the diagonals above the next step's range
+// are complete: they leave the ring into this tile's partial row, each
+// written exactly once (never-touched diagonals are written as zero).
 template <int D, int MASK, int MOD, bool BM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdArgs a) {
   constexpr int BN = 64, NT = BN / 32;
@@ -309,6 +335,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int KC = D / 16, DT = D / 32;
   __shared__ __attribute__((aligned(16))) char sK0[TILE], sV0[TILE], sK1[TILE], sV1[TILE];
   __shared__ __attribute__((aligned(16))) int sD0[BN], sD1[BN];
+  // Relative bias: diagonals of one step (128 + BN - 1 = 191 entries, 3 chunks).
+  constexpr bool REL = MOD == MOD_REL_BIAS;
+  __shared__ __attribute__((aligned(16))) float sB0[REL ? 192 : 1], sB1[REL ? 192 : 1];
+  // Gradient slices [stage][wave][half][96] and the ring of open diagonals.
+  constexpr int GS = 96;
+  __shared__ __attribute__((aligned(16))) float sG[REL ? 2 * 8 * GS : 1], sRing[REL ? 256 : 1];
 
   int b, hq, qt;
   decode_work(blockIdx.x, a.B, a.Hq, a.Hkv, a.n_qt,
@@ -342,6 +374,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     doc_i = row_ok ? doc[qi] : -1;
   }
   const float slope = head_slope<MOD>(a.mod, hq, a.Hq);
+  const int tlen = Sq + Skv - 1;
+  const float* T = nullptr;
+  if constexpr (REL) T = uniform_ptr(a.mod.rel_bias + (size_t)hq * tlen);
+  const bool want_grad = REL && a.mod.rel_bias_part != nullptr;
 
   constexpr int STEPS_PER_BLOCK = kMaskBlock / BN;
   int step_lo = 0, n_steps = 0;
@@ -371,23 +407,74 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return blk * BN;
   };
 
-  auto issue = [&](int k0, char* kn, char* vn, int* dn) {
+  auto issue = [&](int k0, char* kn, char* vn, int* dn, float* bn) {
     tile_load<D, BN>(rows_rsrc(K, Skv, k0, ROW), kn, wave, lane);
     tile_load<D, BN>(rows_rsrc(V, Skv, k0, ROW), vn, wave, lane);
     if constexpr (MASK == MASK_DOCUMENT) {
       if (wave == 0) ints_to_lds(doc, Skv, k0, dn, lane);
     }
+    if constexpr (REL) {
+      // Entry e: i - j = q0 - k0 - (BN - 1) + e.
+      if (wave < 3) bias_chunk_to_lds(T, tlen, q0 - k0 - (BN - 1) + (Skv - 1), bn, wave, lane);
+    }
+  };
+
+  // ---- relative-bias gradient: this tile's partial row and its flushes
+  float* part = nullptr;
+  if constexpr (REL) {
+    if (want_grad) part = a.mod.rel_bias_part + ((size_t)(b * a.Hq + hq) * a.n_qt + qt) * (size_t)(Skv + kBiasRowPad);
+  }
+  int open_hi = q0 + kTileQ - 1;  // highest diagonal not yet written to the partial row
+  // Close the step that started at key kp (its slices in g): diagonals above
+  // next_hi are final.  Also writes zeros for never-touched diagonals in
+  // (next_hi, open_hi].  Entry d of the row sits at d - q0 + Skv - 1.
+  auto flush = [&](float* g, int kp, int next_hi) {
+    const int lo = q0 - kp - (BN - 1), hi = q0 + kTileQ - 1 - kp;
+    if (tid < kTileQ + BN - 1) {
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int e = tid - 32 * w;
+        if (e >= 0 && e < 32 + BN - 1) {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            float* x = g + (2 * w + h2) * GS + e;
+            v += *x;
+            *x = 0.0f;
+          }
+        }
+      }
+      const int d = lo + tid;
+      float* r = sRing + (d & 255);
+      if (d > next_hi) {
+        const int pos = d - q0 + Skv - 1;
+        if (pos >= 0) part[pos] = *r + v;
+        *r = 0.0f;
+      } else {
+        *r += v;
+      }
+    }
+    for (int d = open_hi - tid; d > next_hi; d -= 256) {
+      const int pos = d - q0 + Skv - 1;
+      if ((d < lo || d > hi) && pos >= 0) part[pos] = 0.0f;
+    }
+    open_hi = next_hi;
   };
 
   f32x16 dq[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x16{};
 
-  int blk_c = 0, blk_n = 0, st_c = 0, st_n = 0;
-  auto step = [&](int s, const char* ks, const char* vs, const int* dcs, char* kn, char* vn, int* dn) {
+  int blk_c = 0, blk_n = 0, st_c = 0, st_n = 0, k_prev = 0;
+  auto step = [&](int s, const char* ks, const char* vs, const int* dcs, const float* bs, float* gs, float* gp,
+                  char* kn, char* vn, int* dn, float* bn) {
     const int k0 = key0(s, blk_c);
     const bool have_next = s + 1 < n_steps;
-    if (have_next) issue(key0(s + 1, blk_n), kn, vn, dn);
+    if (have_next) issue(key0(s + 1, blk_n), kn, vn, dn, bn);
+    if constexpr (REL) {
+      if (want_grad && s > 0) flush(gp, k_prev, q0 + kTileQ - 1 - k0);
+      k_prev = k0;
+    }
     const int blk_nn = fetch_blk(s + 2);
     if constexpr (BM) st_n = have_next ? bm_state[blk_n] : 0;
     int cls;
@@ -401,6 +488,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (cls != TILE_EMPTY) {
       const int ch = 2 * g16 + ((gi & 3) >> 1);
       const int half = (gi & 1) * 8;
+      // bl[59 - c]: bias of key k0 + c + 4hh; gl[59 - c]: its gradient slot
+      // in this (wave, half-wave) slice (c = 32t + 8(r/4) + r%4).
+      const float* bl = bs + (32 * wave + l32 + 4 - 4 * hh);
+      float* gl = gs + (2 * wave + hh) * GS + (l32 + 4 - 4 * hh);
       // One 32-key subtile at a time keeps the live registers low.
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -416,10 +507,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) {
-            const int jr = 32 * t + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+            const int c = 32 * t + 8 * (rr >> 2) + (rr & 3);
+            const int jr = c + 4 * hh;
             const int j = k0 + jr;
             float p, grad;
-            recompute_p<MOD>(st[rr], qi, j, slope, a, lse2, p, grad);
+            recompute_p<MOD>(st[rr], qi, j, slope, REL ? bl[59 - c] : 0.0f, a, lse2, p, grad);
             if constexpr (MASKED) {
               int dj = 0;
               if constexpr (MASK == MASK_DOCUMENT) dj = dcs[jr];
@@ -427,6 +519,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
               p = ok ? p : 0.0f;
             }
             dpt[rr] = p * (dpt[rr] - del) * grad;
+            if constexpr (REL) {
+              if (want_grad) __hip_atomic_fetch_add(gl + (59 - c), dpt[rr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
           }
         };
         if (cls == TILE_PARTIAL) {
@@ -456,14 +551,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   blk_c = fetch_blk(0);
   blk_n = fetch_blk(1);
   if constexpr (BM) st_c = n_steps > 0 ? bm_state[blk_c] : 0;
+  if constexpr (REL) {
+    if (want_grad) {
+      for (int x = tid; x < 2 * 8 * GS; x += 256) sG[x] = 0.0f;
+      sRing[tid] = 0.0f;
+    }
+  }
   if (n_steps > 0) {
-    issue(key0(0, blk_c), sK0, sV0, sD0);
+    issue(key0(0, blk_c), sK0, sV0, sD0, sB0);
     wait_loads();
   }
   __syncthreads();
   for (int s = 0; s < n_steps; s += 2) {
-    step(s, sK0, sV0, sD0, sK1, sV1, sD1);
-    if (s + 1 < n_steps) step(s + 1, sK1, sV1, sD1, sK0, sV0, sD0);
+    step(s, sK0, sV0, sD0, sB0, sG, sG + 8 * GS, sK1, sV1, sD1, sB1);
+    if (s + 1 < n_steps) step(s + 1, sK1, sV1, sD1, sB1, sG + 8 * GS, sG, sK0, sV0, sD0, sB0);
+  }
+  if constexpr (REL) {
+    if (want_grad) {
+      // Close the last step (its slices are in stage (n_steps - 1) & 1) and
+      // write every remaining diagonal down to q0 - Skv + 1.
+      if (n_steps > 0) {
+        flush(sG + ((n_steps - 1) & 1) * 8 * GS, k_prev, q0 - Skv);
+      } else {
+        for (int d = open_hi - tid; d > q0 - Skv; d -= 256) part[d - q0 + Skv - 1] = 0.0f;
+      }
+    }
   }
 
   if (row_ok) {
@@ -477,6 +589,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                    pack_bf16(dq[dt][4 * rq + 2] * a.scale, dq[dt][4 * rq + 3] * a.scale)};
       }
   }
+}
+
+// ---------------------------------------------------------------- bias gradient
+// grad[h][r] = sum over batches b and query tiles qt of the dQ workgroups'
+// partial rows, entry r - 128 qt of row (b, h, qt), in that fixed order, so
+// the result is deterministic.  Tile qt's row covers table entries
+// [128 qt, 128 qt + Skv + 126].  (Templated on the head dimension only so
+// that each translation unit has its own instance.)
+template <int D>
+__global__ __launch_bounds__(256) void bias_grad_reduce_kernel(const float* __restrict__ part,
+                                                               float* __restrict__ grad, int B, int Hq, int n_qt,
+                                                               int Skv, int tlen, int blocks_per_head) {
+  const int h = blockIdx.x / blocks_per_head;
+  const int r = (blockIdx.x - h * blocks_per_head) * 256 + threadIdx.x;
+  if (r >= tlen) return;
+  const size_t row = (size_t)Skv + kBiasRowPad;
+  const int first = r - (Skv + kTileQ - 2);
+  const int qt_lo = first > 0 ? (first + kTileQ - 1) / kTileQ : 0;
+  const int qt_hi = min(n_qt - 1, r / kTileQ);
+  float s = 0.0f;
+  for (int b = 0; b < B; ++b) {
+    const float* p = part + (size_t)(b * Hq + h) * n_qt * row;
+    for (int qt = qt_lo; qt <= qt_hi; ++qt) s += p[(size_t)qt * row + (r - qt * kTileQ)];
+  }
+  grad[(size_t)h * tlen + r] = s;
 }
 
 template <int D, int MASK, int MOD, bool BM>
@@ -500,7 +637,19 @@ static hipError_t launch_bwd_mm(const BwdArgs& a, int phases, hipStream_t st) {
   if ((phases & 4) && rows > 0) {
     hipLaunchKernelGGL((bwd_dq_kernel<D, MASK, MOD, BM>), dim3((unsigned)(a.B * a.Hq * a.n_qt)), dim3(256), 0, st,
                        a);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if constexpr (MOD == MOD_REL_BIAS) {
+    // The table gradient (also when there are no rows: then it is zero).
+    const int tlen = a.Sq + a.Skv - 1;
+    if ((phases & 4) && a.mod.rel_bias_grad != nullptr && tlen > 0) {
+      const int per_head = (tlen + 255) / 256;
+      hipLaunchKernelGGL((bias_grad_reduce_kernel<D>), dim3((unsigned)(a.Hq * per_head)), dim3(256), 0, st,
+                         a.mod.rel_bias_part, a.mod.rel_bias_grad, rows > 0 ? a.B : 0, a.Hq, a.n_qt, a.Skv, tlen,
+                         per_head);
+      return hipGetLastError();
+    }
   }
   return hipSuccess;
 }
@@ -517,6 +666,7 @@ static hipError_t launch_bwd_mask(const BwdArgs& a, int mod, int phases, hipStre
     case MOD_NONE: return launch_bwd_bm<D, MASK, MOD_NONE>(a, phases, st);
     case MOD_ALIBI: return launch_bwd_bm<D, MASK, MOD_ALIBI>(a, phases, st);
     case MOD_SOFTCAP: return launch_bwd_bm<D, MASK, MOD_SOFTCAP>(a, phases, st);
+    case MOD_REL_BIAS: return launch_bwd_bm<D, MASK, MOD_REL_BIAS>(a, phases, st);
     default: return launch_bwd_bm<D, MASK, MOD_BOOST>(a, phases, st);
   }
 }

@@ -146,6 +146,19 @@ __device__ __forceinline__ void ints_to_lds(const void* src, int n, int i0, int*
                                             (uint32_t)(lane * 4), 0, 0, 0);
 }
 
+// Chunk c (64 floats) of a slice table[i0 .. ) of a relative-position bias
+// table into dst[64 c .. 64 c + 63], by one wave, straight to LDS.  Entries
+// outside [0, len) read as zero: i0 may be negative (the slice of a key tile
+// that runs past the last key), and such lanes get an offset past the end of
+// the resource.  i0 is wave-uniform; `table` must be in scalar registers.
+__device__ __forceinline__ void bias_chunk_to_lds(const float* table, int len, int i0, float* dst, int c, int lane) {
+  const int base = i0 > 0 ? i0 : 0;
+  const int idx = i0 + 64 * c + lane;
+  const uint32_t off = idx >= base ? (uint32_t)(idx - base) * 4u : 0x7ffffff0u;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(table, len, base, 4),
+                                            (__attribute__((address_space(3))) void*)(dst + 64 * c), 4, off, 0, 0, 0);
+}
+
 // Wait until every load this wave issued has landed (vmcnt = 0).
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
 

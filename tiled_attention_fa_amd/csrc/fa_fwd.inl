@@ -56,6 +56,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(16))) char sK0[TILE], sV0[TILE];
   __shared__ __attribute__((aligned(16))) char sK1[F32 ? 16 : TILE], sV1[F32 ? 16 : TILE];
   __shared__ __attribute__((aligned(16))) int sD0[BN], sD1[BN];
+  // Relative-bias diagonals of one key step: 128 + BN - 1 entries, in 64-float chunks.
+  constexpr bool REL = MOD == MOD_REL_BIAS;
+  constexpr int NB = (kTileQ + BN + 62) / 64 * 64;
+  __shared__ __attribute__((aligned(16))) float sB0[REL ? NB : 1], sB1[REL && !F32 ? NB : 1];
 
   int b, hq, qt;
   decode_work(blockIdx.x, a.B, a.Hq, a.Hkv, a.n_qt,
@@ -67,6 +71,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int Sq = a.Sq, Skv = a.Skv;
   const int q0 = qt * kTileQ;
   const int qw0 = q0 + wave * 32;
+  const int tlen = Sq + Skv - 1;
+  const float* T = nullptr;
+  if constexpr (REL) T = uniform_ptr(a.mod.rel_bias + (size_t)hq * tlen);
+  // First table entry of the bias slice of the key step at k0.
+  auto bias_i0 = [&](int k0) { return q0 - k0 - (BN - 1) + (Skv - 1); };
   const int qi = qw0 + l32;
   const bool row_ok = qi < Sq;
   const int window = a.mask.window;
@@ -130,12 +139,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // ---- tile loads.  bf16: straight from memory into an LDS stage (buffer
   // loads, zero past Skv).  fp32: through registers into the single stage.
-  auto issue = [&](int k0, char* ks, char* vs, int* ds) {
+  auto issue = [&](int k0, char* ks, char* vs, int* ds, float* bs) {
     if constexpr (!F32) {
       tile_load<D, BN>(rows_rsrc(K, Skv, k0, D * 2), ks, wave, lane);
       tile_load<D, BN>(rows_rsrc(V, Skv, k0, D * 2), vs, wave, lane);
       if constexpr (MASK == MASK_DOCUMENT) {
         if (wave == 0) ints_to_lds(doc, Skv, k0, ds, lane);
+      }
+      if constexpr (REL) {
+        if (wave < NB / 64) bias_chunk_to_lds(T, tlen, bias_i0(k0), bs, wave, lane);
       }
     }
   };
@@ -153,6 +165,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if constexpr (MASK == MASK_DOCUMENT) {
         if (tid < BN) dr = (k0 + tid < Skv) ? doc[k0 + tid] : -2;
       }
+      float br = 0.0f;
+      if constexpr (REL) {
+        const int idx = bias_i0(k0) + tid;
+        if (tid < NB && idx >= 0 && idx < tlen) br = T[idx];
+      }
 #pragma unroll
       for (int p = 0; p < LOADS; ++p) {
         const int id = tid + 256 * p, r = id / NCH, c = id % NCH;
@@ -166,6 +183,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       if constexpr (MASK == MASK_DOCUMENT) {
         if (tid < BN) sD0[tid] = dr;
+      }
+      if constexpr (REL) {
+        if (tid < NB) sB0[tid] = br;
       }
     }
   };
@@ -182,10 +202,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // (list entry two steps ahead, state one step ahead) are issued after the
   // tile loads and only consumed in the next step, after its wait.
   int blk_c = 0, blk_n = 0, st_c = 0, st_n = 0;
-  auto step = [&](int s, const char* ks, const char* vs, const int* ds, char* kn, char* vn, int* dn) {
+  auto step = [&](int s, const char* ks, const char* vs, const int* ds, const float* bs, char* kn, char* vn, int* dn,
+                  float* bn) {
     const int k0 = key0(s, blk_c);
     const bool have_next = s + 1 < n_steps;
-    if (have_next) issue(key0(s + 1, blk_n), kn, vn, dn);
+    if (have_next) issue(key0(s + 1, blk_n), kn, vn, dn, bn);
     const int blk_nn = fetch_blk(s + 2);
     if constexpr (BM) st_n = have_next ? bm_state[blk_n] : 0;
     if (k0 < Skv) ++visited;
@@ -229,9 +250,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
-      // ---- scores to log2 units, modifier, mask; block max
+      // ---- scores to log2 units (relative bias: natural units), modifier, mask; block max
       float mb = kNegInf;
       const bool plain = (MOD == MOD_NONE) && cls == TILE_FULL;
+      // bl[CMAX - c] is the bias of key k0 + c + 4hh (c = 32t + 8(r/4) + r%4).
+      constexpr int CMAX = 32 * (NT - 1) + 27;
+      const float* bl = bs + (32 * wave + l32 + 4 - 4 * hh);
       if (plain) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -243,11 +267,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int t = 0; t < NT; ++t)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int jr = 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const int c = 32 * t + 8 * (r >> 2) + (r & 3);
+            const int jr = c + 4 * hh;
             const int j = k0 + jr;
             float x;
             if constexpr (MOD == MOD_NONE) {
               x = st[t][r] * a.scale_log2;
+            } else if constexpr (REL) {
+              x = __builtin_fmaf(st[t][r], a.scale, bl[CMAX - c]);
             } else {
               x = apply_mod<MOD>(st[t][r] * a.scale, qi, j, slope, a.mod) * kLog2e;
             }
@@ -260,14 +287,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             st[t][r] = x;
             mb = fmaxf(mb, x);
           }
+        if constexpr (REL) mb *= kLog2e;
       }
       mb = half_swap_max(mb);
       const float m_new = fmaxf(m, mb);
       const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
       const float alpha = fast_exp2(m - m_use);
       // ---- probabilities, row sum
-      // Plain tiles still hold raw scores; the others are already in log2 units.
-      const float mult = plain ? a.scale_log2 : 1.0f;
+      // Plain tiles still hold raw scores, relative-bias scores are in natural
+      // units, the others are already in log2 units.
+      const float mult = plain ? a.scale_log2 : (REL ? kLog2e : 1.0f);
       float ps = 0.0f;
 #pragma unroll
       for (int t = 0; t < NT; ++t)
@@ -354,17 +383,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if constexpr (F32) {
       load_f32(key0(0, blk_c));
     } else {
-      issue(key0(0, blk_c), sK0, sV0, sD0);
+      issue(key0(0, blk_c), sK0, sV0, sD0, sB0);
       wait_loads();
     }
   }
   __syncthreads();
   if constexpr (F32) {
-    for (int s = 0; s < n_steps; ++s) step(s, sK0, sV0, sD0, sK0, sV0, sD0);
+    for (int s = 0; s < n_steps; ++s) step(s, sK0, sV0, sD0, sB0, sK0, sV0, sD0, sB0);
   } else {
     for (int s = 0; s < n_steps; s += 2) {
-      step(s, sK0, sV0, sD0, sK1, sV1, sD1);
-      if (s + 1 < n_steps) step(s + 1, sK1, sV1, sD1, sK0, sV0, sD0);
+      step(s, sK0, sV0, sD0, sB0, sK1, sV1, sD1, sB1);
+      if (s + 1 < n_steps) step(s + 1, sK1, sV1, sD1, sB1, sK0, sV0, sD0, sB0);
     }
   }
 
@@ -418,7 +447,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int BN = 64, NT = 2, ROW = D * 2, TILE = BN * ROW;
   constexpr int DT = D / 32, KC = D / 16;
   constexpr int QT = 2 * kTileQ;  // query rows per workgroup
+  constexpr bool REL = MOD == MOD_REL_BIAS;
   __shared__ __attribute__((aligned(16))) char sK0[TILE], sK1[TILE], sV0[TILE], sV1[TILE];
+  // Relative-bias diagonals of one key step: QT + BN - 1 entries (5 chunks of 64).
+  __shared__ __attribute__((aligned(16))) float sB0[REL ? 320 : 1], sB1[REL ? 320 : 1];
 
   int b, hq, qt;
   decode_work(blockIdx.x, a.B, a.Hq, a.Hkv, (a.Sq + QT - 1) / QT, MASK == MASK_CAUSAL, b, hq, qt);
@@ -433,6 +465,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const uint16_t* K = uniform_ptr((const uint16_t*)a.k + (size_t)(b * a.Hkv + hk) * Skv * D);
   const uint16_t* V = uniform_ptr((const uint16_t*)a.v + (size_t)(b * a.Hkv + hk) * Skv * D);
   const float slope = head_slope<MOD>(a.mod, hq, a.Hq);
+  const int tlen = Sq + Skv - 1;
+  const float* T = nullptr;
+  if constexpr (REL) T = uniform_ptr(a.mod.rel_bias + (size_t)hq * tlen);
 
   u32x4 qf[KC];
   {
@@ -458,6 +493,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Tile loads are issued by the 4 waves of group 0.
   auto issue_k = [&](int j, char* ks) { tile_load<D, BN>(rows_rsrc(K, Skv, (step_lo + j) * BN, ROW), ks, wave & 3, lane); };
   auto issue_v = [&](int j, char* vs) { tile_load<D, BN>(rows_rsrc(V, Skv, (step_lo + j) * BN, ROW), vs, wave & 3, lane); };
+  // Bias diagonals of step j (entry e: i - j = q0 - k0 - (BN - 1) + e), by
+  // the 4 waves of group 1, which issue no tile loads.
+  auto issue_b = [&](int j, float* bs) {
+    const int i0 = q0 - (step_lo + j) * BN - (BN - 1) + (Skv - 1);
+    bias_chunk_to_lds(T, tlen, i0, bs, wave & 3, lane);
+    if ((wave & 3) == 0) bias_chunk_to_lds(T, tlen, i0, bs, 4, lane);
+  };
 
   float m = kNegInf, l = 0.0f;  // running max (log2 units), this lane's partial row sum
   f32x16 acc[DT];
@@ -517,9 +559,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   // Softmax of step j's scores: running max, rescale of O, P packed to bf16.
-  auto v_phase = [&](int j) __attribute__((always_inline)) {
+  // With the relative bias, scores stay in natural units until the exp.
+  auto v_phase = [&](int j, const float* bs) __attribute__((always_inline)) {
     if (j < 0 || j >= n_steps || cls_s == TILE_EMPTY) return;
     const int k0 = (step_lo + j) * BN;
+    // bl[59 - c] is the bias of key k0 + c + 4hh (c = 32t + 8(r/4) + r%4).
+    const float* bl = bs + (qi - q0 + 4 - 4 * hh);
     float mb = kNegInf;
     const bool plain = (MOD == MOD_NONE) && cls_s == TILE_FULL;
     if (plain) {
@@ -533,10 +578,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j2 = k0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const int c = 32 * t + 8 * (r >> 2) + (r & 3);
+          const int j2 = k0 + c + 4 * hh;
           float x;
           if constexpr (MOD == MOD_NONE) {
             x = st[t][r] * a.scale_log2;
+          } else if constexpr (REL) {
+            x = __builtin_fmaf(st[t][r], a.scale, bl[59 - c]);
           } else {
             x = apply_mod<MOD>(st[t][r] * a.scale, qi, j2, slope, a.mod) * kLog2e;
           }
@@ -547,13 +595,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           st[t][r] = x;
           mb = fmaxf(mb, x);
         }
+      if constexpr (REL) mb *= kLog2e;
     }
     mb = half_swap_max(mb);
     const float m_new = fmaxf(m, mb);
     const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
     const float alpha = fast_exp2(m - m_use);
-    // Plain tiles still hold raw scores; the others are already in log2 units.
-    const float mult = plain ? a.scale_log2 : 1.0f;
+    // Plain tiles still hold raw scores, relative-bias scores are in natural
+    // units, the others are already in log2 units.
+    const float mult = plain ? a.scale_log2 : (REL ? kLog2e : 1.0f);
     float ps = 0.0f;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -579,26 +629,35 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                           pack_bf16(st[t][8 * cc + 4], st[t][8 * cc + 5]), pack_bf16(st[t][8 * cc + 6], st[t][8 * cc + 7])};
   };
 
-  // Step j of this wave.  (kc: K_j, vp: V_{j-1}; kn, vc: where K_{j+1}, V_j go.)
-  auto step = [&](int j, const char* kc, const char* vp, char* kn, char* vc) __attribute__((always_inline)) {
+  // Step j of this wave.  (kc: K_j, vp: V_{j-1}; kn, vc: where K_{j+1}, V_j
+  // go; bc: bias of step j; bn: where group 1 loads the bias of step j + 1.
+  // Group 1 is half a step behind, so that slot's last readers, the softmax
+  // phases of step j - 1, are done when it starts its step j.)
+  auto step = [&](int j, const char* kc, const char* vp, char* kn, char* vc, const float* bc, float* bn)
+      __attribute__((always_inline)) {
     if (grp == 0) {
       if (j + 1 < n_steps) issue_k(j + 1, kn);
       if (j < n_steps) issue_v(j, vc);
+    } else if constexpr (REL) {
+      if (j + 1 < n_steps) issue_b(j + 1, bn);
     }
     m_phase(j, kc, vp);
     phase_barrier();
-    v_phase(j);
+    v_phase(j, bc);
     wait_loads();
     phase_barrier();
   };
 
   if (grp == 0 && n_steps > 0) issue_k(0, sK0);
+  if constexpr (REL) {
+    if (grp == 1 && n_steps > 0) issue_b(0, sB0);
+  }
   wait_loads();
   __syncthreads();
   if (grp == 1) phase_barrier();
   for (int j = 0; j <= n_steps; j += 2) {
-    step(j, sK0, sV1, sK1, sV0);
-    if (j + 1 <= n_steps) step(j + 1, sK1, sV0, sK0, sV1);
+    step(j, sK0, sV1, sK1, sV0, sB0, sB1);
+    if (j + 1 <= n_steps) step(j + 1, sK1, sV0, sK0, sV1, sB1, sB0);
   }
   if (grp == 0) phase_barrier();
 
@@ -636,6 +695,7 @@ static hipError_t launch_pp(const FwdArgs& a, int mod, hipStream_t st) {
     case MOD_NONE: hipLaunchKernelGGL((fwd_pp_kernel<D, MASK, MOD_NONE>), grid, block, 0, st, a); break;
     case MOD_ALIBI: hipLaunchKernelGGL((fwd_pp_kernel<D, MASK, MOD_ALIBI>), grid, block, 0, st, a); break;
     case MOD_SOFTCAP: hipLaunchKernelGGL((fwd_pp_kernel<D, MASK, MOD_SOFTCAP>), grid, block, 0, st, a); break;
+    case MOD_REL_BIAS: hipLaunchKernelGGL((fwd_pp_kernel<D, MASK, MOD_REL_BIAS>), grid, block, 0, st, a); break;
     default: hipLaunchKernelGGL((fwd_pp_kernel<D, MASK, MOD_BOOST>), grid, block, 0, st, a); break;
   }
   return hipGetLastError();
@@ -648,6 +708,7 @@ static hipError_t launch_mod(const FwdArgs& a, int mod, hipStream_t st) {
     case MOD_NONE: hipLaunchKernelGGL((fwd_kernel<D, F32, MASK, MOD_NONE, BM>), grid, block, 0, st, a); break;
     case MOD_ALIBI: hipLaunchKernelGGL((fwd_kernel<D, F32, MASK, MOD_ALIBI, BM>), grid, block, 0, st, a); break;
     case MOD_SOFTCAP: hipLaunchKernelGGL((fwd_kernel<D, F32, MASK, MOD_SOFTCAP, BM>), grid, block, 0, st, a); break;
+    case MOD_REL_BIAS: hipLaunchKernelGGL((fwd_kernel<D, F32, MASK, MOD_REL_BIAS, BM>), grid, block, 0, st, a); break;
     default: hipLaunchKernelGGL((fwd_kernel<D, F32, MASK, MOD_BOOST, BM>), grid, block, 0, st, a); break;
   }
   return hipGetLastError();
