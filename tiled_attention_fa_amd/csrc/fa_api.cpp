@@ -29,6 +29,16 @@ int check_shapes(int B, int Hq, int Hkv, int Sq, int Skv, int D) {
   return FA_OK;
 }
 
+// scale * log2(e), the multiplier from raw scores to log2 units.  A zero
+// scale maps to the smallest normal-range positive value used here, 1e-30:
+// the kernels may then keep masked raw scores at -inf (-inf * 0 would be NaN),
+// and every admissible probability still rounds to exactly 1 (|s| * 1e-30 is
+// far below fp32 resolution), as with a zero scale.
+float log2_multiplier(float scale) {
+  const float c = (float)((double)scale * 1.4426950408889634);
+  return c > 0.0f ? c : 1e-30f;
+}
+
 // Checks shared by the forward and backward passes; fills the mask and
 // modifier argument blocks.
 int check_variant(int B, int Hq, int Sq, int Skv, float scale, int mask_kind, const fa_mask_params* mp,
@@ -168,7 +178,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, i
   a.Skv = Skv;
   a.n_qt = (int)cdiv(Sq, kTileQ);
   a.scale = scale;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.scale_log2 = log2_multiplier(scale);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (dtype == FA_BF16)
@@ -236,7 +246,7 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const uint8_t* q_
   a.D = D;
   a.n_qt = (int)cdiv(Sq, kTileQ);
   a.window = mask.window;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.scale_log2 = log2_multiplier(scale);
   const hipError_t e = launch_fp8_fwd(a, mask_kind, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -313,7 +323,7 @@ int fa_bwd_phase(int phase, const void* q, const void* k, const void* v, const v
   a.n_qt = (int)cdiv(Sq, kTileQ);
   a.n_kt = (int)cdiv(Skv, kTileQ);
   a.scale = scale;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.scale_log2 = log2_multiplier(scale);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e = D == 128 ? launch_bwd_d<128>(a, mask_kind, score_mod_kind, phase, st)
                                 : launch_bwd_d<64>(a, mask_kind, score_mod_kind, phase, st);

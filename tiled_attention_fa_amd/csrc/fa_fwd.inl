@@ -252,11 +252,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       // ---- scores to log2 units (relative bias: natural units), modifier, mask; block max
       float mb = kNegInf;
-      const bool plain = (MOD == MOD_NONE) && cls == TILE_FULL;
       // bl[CMAX - c] is the bias of key k0 + c + 4hh (c = 32t + 8(r/4) + r%4).
       constexpr int CMAX = 32 * (NT - 1) + 27;
       const float* bl = bs + (32 * wave + l32 + 4 - 4 * hh);
-      if (plain) {
+      if constexpr (MOD == MOD_NONE) {
+        // Raw scores stay raw: masked entries become -inf in place (the log2
+        // multiplier is > 0), and the multiplier folds into the exponent's FMA.
+        if (cls == TILE_PARTIAL) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int jr = 32 * t + 8 * (r >> 2) + (r & 3) + 4 * hh;
+              const int j = k0 + jr;
+              int dj = 0;
+              if constexpr (MASK == MASK_DOCUMENT) dj = ds[jr];
+              const bool ok = j < Skv && mask_ok<MASK>(qi, j, window, doc_i, dj);
+              st[t][r] = ok ? st[t][r] : kNegInf;
+            }
+        }
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -271,9 +285,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int jr = c + 4 * hh;
             const int j = k0 + jr;
             float x;
-            if constexpr (MOD == MOD_NONE) {
-              x = st[t][r] * a.scale_log2;
-            } else if constexpr (REL) {
+            if constexpr (REL) {
               x = __builtin_fmaf(st[t][r], a.scale, bl[CMAX - c]);
             } else {
               x = apply_mod<MOD>(st[t][r] * a.scale, qi, j, slope, a.mod) * kLog2e;
@@ -294,9 +306,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
       const float alpha = fast_exp2(m - m_use);
       // ---- probabilities, row sum
-      // Plain tiles still hold raw scores, relative-bias scores are in natural
-      // units, the others are already in log2 units.
-      const float mult = plain ? a.scale_log2 : (REL ? kLog2e : 1.0f);
+      // Unmodified scores are raw, relative-bias scores in natural units, the
+      // others already in log2 units.
+      const float mult = MOD == MOD_NONE ? a.scale_log2 : (REL ? kLog2e : 1.0f);
       float ps = 0.0f;
 #pragma unroll
       for (int t = 0; t < NT; ++t)
@@ -566,8 +578,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // bl[59 - c] is the bias of key k0 + c + 4hh (c = 32t + 8(r/4) + r%4).
     const float* bl = bs + (qi - q0 + 4 - 4 * hh);
     float mb = kNegInf;
-    const bool plain = (MOD == MOD_NONE) && cls_s == TILE_FULL;
-    if (plain) {
+    if constexpr (MOD == MOD_NONE) {
+      // Raw scores stay raw: masked entries become -inf in place (the log2
+      // multiplier is > 0, so they stay -inf), and the multiplier folds into
+      // the exponent's FMA.  One register flow for full and partial tiles.
+      if (cls_s == TILE_PARTIAL) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j2 = k0 + 32 * t + 8 * (r >> 2) + (r & 3) + 4 * hh;
+            const bool ok = j2 < Skv && mask_ok<MASK>(qi, j2, window, 0, 0);
+            st[t][r] = ok ? st[t][r] : kNegInf;
+          }
+      }
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -581,9 +605,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           const int c = 32 * t + 8 * (r >> 2) + (r & 3);
           const int j2 = k0 + c + 4 * hh;
           float x;
-          if constexpr (MOD == MOD_NONE) {
-            x = st[t][r] * a.scale_log2;
-          } else if constexpr (REL) {
+          if constexpr (REL) {
             x = __builtin_fmaf(st[t][r], a.scale, bl[59 - c]);
           } else {
             x = apply_mod<MOD>(st[t][r] * a.scale, qi, j2, slope, a.mod) * kLog2e;
@@ -601,9 +623,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float m_new = fmaxf(m, mb);
     const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
     const float alpha = fast_exp2(m - m_use);
-    // Plain tiles still hold raw scores, relative-bias scores are in natural
-    // units, the others are already in log2 units.
-    const float mult = plain ? a.scale_log2 : (REL ? kLog2e : 1.0f);
+    // Unmodified scores are raw, relative-bias scores in natural units, the
+    // others already in log2 units.
+    const float mult = MOD == MOD_NONE ? a.scale_log2 : (REL ? kLog2e : 1.0f);
     float ps = 0.0f;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
