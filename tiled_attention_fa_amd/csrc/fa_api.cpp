@@ -45,7 +45,7 @@ int check_variant(int B, int Hq, int Sq, int Skv, float scale, int mask_kind, co
                   int mod_kind, const fa_mod_params* op, MaskArgs& mask, ModArgs& mod) {
   if (!std::isfinite(scale) || scale < 0.0f) return FA_ERR_PARAM;
   mask = MaskArgs{0, nullptr};
-  mod = ModArgs{nullptr, 1.0f, 1.0f, 0, 1.0f, nullptr, nullptr, nullptr};
+  mod = ModArgs{nullptr, 1.0f, 1.0f, 0, 1.0f, nullptr, nullptr, nullptr, 0.0f, -1.0f};
   switch (mask_kind) {
     case FA_MASK_NONE:
     case FA_MASK_CAUSAL: break;
@@ -75,6 +75,8 @@ int check_variant(int B, int Hq, int Sq, int Skv, float scale, int mask_kind, co
       if (!std::isfinite(op->softcap) || !(op->softcap > 0.0f)) return FA_ERR_PARAM;
       mod.softcap = op->softcap;
       mod.inv_softcap = 1.0f / op->softcap;
+      mod.softcap_k = (float)(2.0 * (double)scale * 1.4426950408889634 / (double)op->softcap);
+      mod.softcap_m = (float)(-2.0 * (double)op->softcap * 1.4426950408889634);
       break;
     case FA_MOD_LOCAL_BOOST:
       if (!op) return FA_ERR_NULL;

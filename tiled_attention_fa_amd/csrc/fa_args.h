@@ -30,6 +30,9 @@ struct ModArgs {
   // kernel) and the gradient itself ([Hq][Sq + Skv - 1], their sum).
   float* rel_bias_part;
   float* rel_bias_grad;
+  // Softcap in the forward's shifted form (see the forward kernels):
+  // k = 2 scale log2(e) / softcap, m = -2 softcap log2(e).
+  float softcap_k, softcap_m;
 };
 
 // A dQ workgroup's partial row covers the diagonals i - j of its 128 query

@@ -27,6 +27,122 @@
 
 namespace miattn {
 
+// ---------------------------------------------------------------- score transform
+// Turns one wave's raw scores of a key step (st[t][r]: query qi of this lane,
+// key k0 + c + 4hh with c = 32t + 8(r/4) + r%4) into values x, in place, and
+// a multiplier `mult` such that a pair's probability against a row max m (log2
+// units) is exp2(x * mult - m); masked pairs get x * mult = -inf.  Returns the
+// lane's max of x * mult (log2 units, before the two half-waves combine).
+// Each modifier takes the form with the fewest vector instructions per score:
+//   none:    x = the raw score, mult = scale log2(e): the scale folds into the
+//            exponent's FMA and masked scores are -inf in raw units;
+//   ALiBi:   x = raw scale log2(e) + slope log2(e) (j - i), the bias from one
+//            per-4-keys base plus one add, mult = 1;
+//   softcap: c tanh(s / c) = c - 2c / (1 + e^(2s/c)) and softmax ignores the
+//            constant c, so x = 1 / (1 + 2^(k raw)), k = 2 scale log2(e) / c,
+//            mult = -2c log2(e) < 0, masked x = +inf, and the row max is
+//            mult * min x (the epilogue adds c back to the LSE);
+//   boost:   steps with no pair in the band |i - j| < radius take the
+//            unmodified form; band steps x = raw scale log2(e) (factor or 1);
+//   relative bias: x = raw scale + T[h][i - j + Skv - 1] (natural units),
+//            mult = log2(e).
+// ok(j, jr): elementwise mask (partial tiles only; jr = c + 4hh).  bias(c):
+// relative-bias entry of in-step key offset c + 4hh.  qw0: first row of the wave.
+template <int MOD, int NT, typename Ok, typename Bias>
+__device__ __forceinline__ float transform_scores(f32x16 (&st)[NT], bool partial, int k0, int qi, int qw0, int hh,
+                                                  float slope, const FwdArgs& a, Ok ok, Bias bias, float& mult) {
+  const float c1 = a.scale_log2;
+  float mb = kNegInf;
+  bool plain = MOD == MOD_NONE;
+  if constexpr (MOD == MOD_BOOST) {
+    const int R = a.mod.boost_radius;
+    plain = !(k0 + 32 * NT - 1 > qw0 - R && k0 < qw0 + 31 + R);
+  }
+  if (plain) {
+    if (partial) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jr = 32 * t + 8 * (r >> 2) + (r & 3) + 4 * hh;
+          st[t][r] = ok(k0 + jr, jr) ? st[t][r] : kNegInf;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mb = fmaxf(mb, st[t][r]);
+    mult = c1;
+    return mb * c1;
+  }
+  // Elementwise mask (partial tiles only), one branch for the whole step.
+  auto mask_all = [&](float masked) __attribute__((always_inline)) {
+    if (partial) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jr = 32 * t + 8 * (r >> 2) + (r & 3) + 4 * hh;
+          st[t][r] = ok(k0 + jr, jr) ? st[t][r] : masked;
+        }
+    }
+  };
+  if constexpr (MOD == MOD_SOFTCAP) {
+    const float k = a.mod.softcap_k;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[t][r] = fast_rcp(1.0f + fast_exp2(st[t][r] * k));
+    mask_all(__builtin_inff());
+    float rmin = __builtin_inff();
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) rmin = fminf(rmin, st[t][r]);
+    mult = a.mod.softcap_m;
+    return rmin * mult;
+  } else {
+    // ALiBi, boost inside the band, relative bias.
+    const float s2 = slope * kLog2e;
+    const float s2e[4] = {0.0f, s2, 2.0f * s2, 3.0f * s2};
+    const int d0 = k0 + 4 * hh - qi;  // j - i at c = 0
+    const float cf = c1 * a.mod.boost_factor;
+    const int R = a.mod.boost_radius;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float bq = 0.0f;
+        if constexpr (MOD == MOD_ALIBI) bq = s2 * (float)(d0 + 32 * t + 8 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q + e, c = 32 * t + 8 * q + e;
+          float x;
+          if constexpr (MOD == MOD_ALIBI) {
+            x = __builtin_fmaf(st[t][r], c1, e ? bq + s2e[e] : bq);
+          } else if constexpr (MOD == MOD_BOOST) {
+            const int d = d0 + c;  // j - i
+            x = st[t][r] * ((unsigned)(d + R - 1) < (unsigned)(2 * R - 1) ? cf : c1);
+          } else {
+            x = __builtin_fmaf(st[t][r], a.scale, bias(c));
+          }
+          st[t][r] = x;
+        }
+      }
+    mask_all(kNegInf);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mb = fmaxf(mb, st[t][r]);
+    if constexpr (MOD == MOD_REL_BIAS) {
+      mult = kLog2e;
+      return mb * kLog2e;
+    }
+    mult = 1.0f;
+    return mb;
+  }
+}
+
 template <bool F32>
 struct FwdCfg {
   static constexpr int BN = F32 ? 32 : 64;  // keys per step
@@ -251,64 +367,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
       // ---- scores to log2 units (relative bias: natural units), modifier, mask; block max
-      float mb = kNegInf;
       // bl[CMAX - c] is the bias of key k0 + c + 4hh (c = 32t + 8(r/4) + r%4).
       constexpr int CMAX = 32 * (NT - 1) + 27;
       const float* bl = bs + (32 * wave + l32 + 4 - 4 * hh);
-      if constexpr (MOD == MOD_NONE) {
-        // Raw scores stay raw: masked entries become -inf in place (the log2
-        // multiplier is > 0), and the multiplier folds into the exponent's FMA.
-        if (cls == TILE_PARTIAL) {
-#pragma unroll
-          for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int jr = 32 * t + 8 * (r >> 2) + (r & 3) + 4 * hh;
-              const int j = k0 + jr;
-              int dj = 0;
-              if constexpr (MASK == MASK_DOCUMENT) dj = ds[jr];
-              const bool ok = j < Skv && mask_ok<MASK>(qi, j, window, doc_i, dj);
-              st[t][r] = ok ? st[t][r] : kNegInf;
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mb = fmaxf(mb, st[t][r]);
-        mb = mb * a.scale_log2;
-      } else {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int c = 32 * t + 8 * (r >> 2) + (r & 3);
-            const int jr = c + 4 * hh;
-            const int j = k0 + jr;
-            float x;
-            if constexpr (REL) {
-              x = __builtin_fmaf(st[t][r], a.scale, bl[CMAX - c]);
-            } else {
-              x = apply_mod<MOD>(st[t][r] * a.scale, qi, j, slope, a.mod) * kLog2e;
-            }
-            if (cls == TILE_PARTIAL) {
-              int dj = 0;
-              if constexpr (MASK == MASK_DOCUMENT) dj = ds[jr];
-              const bool ok = j < Skv && mask_ok<MASK>(qi, j, window, doc_i, dj);
-              x = ok ? x : kNegInf;
-            }
-            st[t][r] = x;
-            mb = fmaxf(mb, x);
-          }
-        if constexpr (REL) mb *= kLog2e;
-      }
+      float mult;
+      float mb = transform_scores<MOD, NT>(
+          st, cls == TILE_PARTIAL, k0, qi, qw0, hh, slope, a,
+          [&](int j, int jr) {
+            int dj = 0;
+            if constexpr (MASK == MASK_DOCUMENT) dj = ds[jr];
+            return j < Skv && mask_ok<MASK>(qi, j, window, doc_i, dj);
+          },
+          [&](int c) { return REL ? bl[CMAX - c] : 0.0f; }, mult);
       mb = half_swap_max(mb);
       const float m_new = fmaxf(m, mb);
       const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
       const float alpha = fast_exp2(m - m_use);
       // ---- probabilities, row sum
-      // Unmodified scores are raw, relative-bias scores in natural units, the
-      // others already in log2 units.
-      const float mult = MOD == MOD_NONE ? a.scale_log2 : (REL ? kLog2e : 1.0f);
       float ps = 0.0f;
 #pragma unroll
       for (int t = 0; t < NT; ++t)
@@ -409,8 +484,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
 
-  // ---- epilogue: O = acc / l, LSE = ln 2 (m + log2 l)
+  // ---- epilogue: O = acc / l, LSE = ln 2 (m + log2 l) (+ the constant the
+  // softcap form leaves out)
   const float lt = half_swap_sum(l);
+  const float lse_shift = MOD == MOD_SOFTCAP ? a.mod.softcap : 0.0f;
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (row_ok) {
     elem_t* Orow = (elem_t*)a.o + ((size_t)(b * a.Hq + hq) * Sq + qi) * D;
@@ -428,7 +505,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     if (a.lse != nullptr && hh == 0)
-      a.lse[(size_t)(b * a.Hq + hq) * Sq + qi] = lt > 0.0f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
+      a.lse[(size_t)(b * a.Hq + hq) * Sq + qi] = lt > 0.0f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 + lse_shift : kNegInf;
   }
   if (a.visited != nullptr && tid == 0) atomicAdd(&a.visited[(size_t)(b * a.Hq + hq) * a.n_qt + qt], visited);
 }
@@ -577,55 +654,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int k0 = (step_lo + j) * BN;
     // bl[59 - c] is the bias of key k0 + c + 4hh (c = 32t + 8(r/4) + r%4).
     const float* bl = bs + (qi - q0 + 4 - 4 * hh);
-    float mb = kNegInf;
-    if constexpr (MOD == MOD_NONE) {
-      // Raw scores stay raw: masked entries become -inf in place (the log2
-      // multiplier is > 0, so they stay -inf), and the multiplier folds into
-      // the exponent's FMA.  One register flow for full and partial tiles.
-      if (cls_s == TILE_PARTIAL) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j2 = k0 + 32 * t + 8 * (r >> 2) + (r & 3) + 4 * hh;
-            const bool ok = j2 < Skv && mask_ok<MASK>(qi, j2, window, 0, 0);
-            st[t][r] = ok ? st[t][r] : kNegInf;
-          }
-      }
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mb = fmaxf(mb, st[t][r]);
-      mb = mb * a.scale_log2;
-    } else {
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = 32 * t + 8 * (r >> 2) + (r & 3);
-          const int j2 = k0 + c + 4 * hh;
-          float x;
-          if constexpr (REL) {
-            x = __builtin_fmaf(st[t][r], a.scale, bl[59 - c]);
-          } else {
-            x = apply_mod<MOD>(st[t][r] * a.scale, qi, j2, slope, a.mod) * kLog2e;
-          }
-          if (cls_s == TILE_PARTIAL) {
-            const bool ok = j2 < Skv && mask_ok<MASK>(qi, j2, window, 0, 0);
-            x = ok ? x : kNegInf;
-          }
-          st[t][r] = x;
-          mb = fmaxf(mb, x);
-        }
-      if constexpr (REL) mb *= kLog2e;
-    }
+    float mult;
+    float mb = transform_scores<MOD, NT>(
+        st, cls_s == TILE_PARTIAL, k0, qi, qw0, hh, slope, a,
+        [&](int j, int) { return j < Skv && mask_ok<MASK>(qi, j, window, 0, 0); },
+        [&](int c) { return REL ? bl[59 - c] : 0.0f; }, mult);
     mb = half_swap_max(mb);
     const float m_new = fmaxf(m, mb);
     const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
     const float alpha = fast_exp2(m - m_use);
-    // Unmodified scores are raw, relative-bias scores in natural units, the
-    // others already in log2 units.
-    const float mult = MOD == MOD_NONE ? a.scale_log2 : (REL ? kLog2e : 1.0f);
     float ps = 0.0f;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -683,8 +720,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   if (grp == 0) phase_barrier();
 
-  // ---- epilogue: O = acc / l, LSE = ln 2 (m + log2 l)
+  // ---- epilogue: O = acc / l, LSE = ln 2 (m + log2 l) (+ the constant the
+  // softcap form leaves out)
   const float lt = half_swap_sum(l);
+  const float lse_shift = MOD == MOD_SOFTCAP ? a.mod.softcap : 0.0f;
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (row_ok) {
     uint16_t* Orow = (uint16_t*)a.o + ((size_t)(b * a.Hq + hq) * Sq + qi) * D;
@@ -697,7 +736,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                      pack_bf16(acc[dt][4 * rq + 2] * inv, acc[dt][4 * rq + 3] * inv)};
       }
     if (a.lse != nullptr && hh == 0)
-      a.lse[(size_t)(b * a.Hq + hq) * Sq + qi] = lt > 0.0f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
+      a.lse[(size_t)(b * a.Hq + hq) * Sq + qi] = lt > 0.0f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 + lse_shift : kNegInf;
   }
   // Debug count per 128-row query tile: key steps holding an admissible pair.
   if (a.visited != nullptr && (tid & 255) == 0 && qg0 < Sq) {
