@@ -46,11 +46,13 @@ namespace miattn {
 //            unmodified form; band steps x = raw scale log2(e) (factor or 1);
 //   relative bias: x = raw scale + T[h][i - j + Skv - 1] (natural units),
 //            mult = log2(e).
-// ok(j, jr): elementwise mask (partial tiles only; jr = c + 4hh).  bias(c):
+// partial: 0 = no masking (full tile), 1 = the pair is admissible iff j < Skv
+// and j <= qi, 2 = admissible iff ok(j, jr) (jr = c + 4hh).  bias(c):
 // relative-bias entry of in-step key offset c + 4hh.  qw0: first row of the wave.
 template <int MOD, int NT, typename Ok, typename Bias>
-__device__ __forceinline__ float transform_scores(f32x16 (&st)[NT], bool partial, int k0, int qi, int qw0, int hh,
-                                                  float slope, const FwdArgs& a, Ok ok, Bias bias, float& mult) {
+__device__ __forceinline__ float transform_scores(f32x16 (&st)[NT], int partial, int k0, int qi, int qw0, int hh,
+                                                  int Skv, float slope, const FwdArgs& a, Ok ok, Bias bias,
+                                                  float& mult) {
   const float c1 = a.scale_log2;
   float mb = kNegInf;
   bool plain = MOD == MOD_NONE;
@@ -58,26 +60,17 @@ __device__ __forceinline__ float transform_scores(f32x16 (&st)[NT], bool partial
     const int R = a.mod.boost_radius;
     plain = !(k0 + 32 * NT - 1 > qw0 - R && k0 < qw0 + 31 + R);
   }
-  if (plain) {
-    if (partial) {
+  // Elementwise mask, one branch per mode for the whole step.
+  auto mask_all = [&](float masked) __attribute__((always_inline)) {
+    if (partial == 1) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int jr = 32 * t + 8 * (r >> 2) + (r & 3) + 4 * hh;
-          st[t][r] = ok(k0 + jr, jr) ? st[t][r] : kNegInf;
+          const int j = k0 + 32 * t + 8 * (r >> 2) + (r & 3) + 4 * hh;
+          st[t][r] = (j < Skv && j <= qi) ? st[t][r] : masked;
         }
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mb = fmaxf(mb, st[t][r]);
-    mult = c1;
-    return mb * c1;
-  }
-  // Elementwise mask (partial tiles only), one branch for the whole step.
-  auto mask_all = [&](float masked) __attribute__((always_inline)) {
-    if (partial) {
+    } else if (partial == 2) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -87,6 +80,15 @@ __device__ __forceinline__ float transform_scores(f32x16 (&st)[NT], bool partial
         }
     }
   };
+  if (plain) {
+    mask_all(kNegInf);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mb = fmaxf(mb, st[t][r]);
+    mult = c1;
+    return mb * c1;
+  }
   if constexpr (MOD == MOD_SOFTCAP) {
     const float k = a.mod.softcap_k;
 #pragma unroll
@@ -370,9 +372,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // bl[CMAX - c] is the bias of key k0 + c + 4hh (c = 32t + 8(r/4) + r%4).
       constexpr int CMAX = 32 * (NT - 1) + 27;
       const float* bl = bs + (32 * wave + l32 + 4 - 4 * hh);
+      // Mask mode: a partial step whose keys and rows all carry one document
+      // id needs only the causal test (the usual case: a diagonal tile inside
+      // a document).  Checked per step from the staged key ids and the rows'.
+      int mode = cls == TILE_PARTIAL ? 2 : 0;
+      if constexpr (MASK == MASK_DOCUMENT) {
+        if (mode == 2) {
+          const int ref = wave_uniform(doc_i);
+          const bool keys_one = __builtin_amdgcn_ballot_w64(lane >= BN || ds[lane] == ref) == ~0ull;
+          const bool rows_one = __builtin_amdgcn_ballot_w64(doc_i == ref) == ~0ull;
+          if (keys_one && rows_one) mode = 1;
+        }
+      } else if constexpr (MASK == MASK_CAUSAL) {
+        mode = mode ? 1 : 0;
+      }
       float mult;
       float mb = transform_scores<MOD, NT>(
-          st, cls == TILE_PARTIAL, k0, qi, qw0, hh, slope, a,
+          st, mode, k0, qi, qw0, hh, Skv, slope, a,
           [&](int j, int jr) {
             int dj = 0;
             if constexpr (MASK == MASK_DOCUMENT) dj = ds[jr];
@@ -656,7 +672,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float* bl = bs + (qi - q0 + 4 - 4 * hh);
     float mult;
     float mb = transform_scores<MOD, NT>(
-        st, cls_s == TILE_PARTIAL, k0, qi, qw0, hh, slope, a,
+        st, cls_s == TILE_PARTIAL ? (MASK == MASK_CAUSAL ? 1 : 2) : 0, k0, qi, qw0, hh, Skv, slope, a,
         [&](int j, int) { return j < Skv && mask_ok<MASK>(qi, j, window, 0, 0); },
         [&](int c) { return REL ? bl[59 - c] : 0.0f; }, mult);
     mb = half_swap_max(mb);
