@@ -183,3 +183,12 @@ def test_visited_counts_analytic():
             ok = oracle.allowed(var, 0, rows, np.arange(S))
             want = sum(1 for kt in range(-(-S // step)) if ok[:, kt * step:(kt + 1) * step].any())
             assert int(vis[0, 0, qt]) == want, (spec, qt, int(vis[0, 0, qt]), want)
+
+
+@pytest.mark.parametrize("spec", [dict(mask=2, window=2200), dict(mask=2, window=2100, mod=1)])
+def test_long_window(spec):
+    """Windows longer than 2048 keys take the 256-row ping-pong kernel (short
+    windows the 128-row kernel): ragged length, several tiles per window."""
+    (o, lse), o_ref, l_ref = run_case(1, 2, 1, 2600, 2600, 128, "bf16", spec, seed=31)
+    check_out(o, o_ref, "bf16")
+    check_lse(lse, l_ref)

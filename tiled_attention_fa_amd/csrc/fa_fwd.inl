@@ -794,7 +794,13 @@ static hipError_t launch_mod(const FwdArgs& a, int mod, hipStream_t st) {
 template <int D, bool F32, int MASK>
 static hipError_t launch_bm(const FwdArgs& a, int mod, hipStream_t st) {
   if (a.bm.tile_state != nullptr) return launch_mod<D, F32, MASK, true>(a, mod, st);
-  if constexpr (!F32 && MASK != MASK_DOCUMENT) return launch_pp<D, MASK>(a, mod, st);
+  // The ping-pong kernel walks the union of the key ranges of 256 rows; for
+  // short windows that union is up to 25% longer than a 128-row tile's
+  // range, and the 4-wave kernel is faster (1024-key window: 0.42 vs
+  // 0.44 ms at B2 Hq32 S8192).
+  if constexpr (!F32 && MASK != MASK_DOCUMENT) {
+    if (MASK != MASK_WINDOW || a.mask.window > 2048) return launch_pp<D, MASK>(a, mod, st);
+  }
   return launch_mod<D, F32, MASK, false>(a, mod, st);
 }
 
