@@ -48,31 +48,31 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 }
 
 // Probability, and the factor that turns dP - delta into dS, for one
-// (query i, key j) score: x2 is the modified score in log2 units.  `bias` is
-// the relative-bias table entry of the pair (MOD_REL_BIAS only).
+// (query i, key j) score: p = 2^(x2 - lse2) with x2 the modified score in
+// log2 units, the subtraction folded into the exponent's FMA.  `bias` is the
+// relative-bias table entry of the pair (MOD_REL_BIAS only).  Softcap uses
+// r = 1 / (1 + 2^(k raw)), k = 2 scale log2(e) / c: tanh(s / c) = 1 - 2r, so
+// x2 = c log2(e) + (-2c log2(e)) r and the derivative 1 - tanh^2 = 4r(1 - r).
 template <int MOD>
 __device__ __forceinline__ void recompute_p(float sraw, int i, int j, float slope, float bias, const BwdArgs& a,
                                             float lse2, float& p, float& grad) {
-  float x2;
   grad = 1.0f;
   if constexpr (MOD == MOD_NONE) {
-    x2 = sraw * a.scale_log2;
+    p = fast_exp2(__builtin_fmaf(sraw, a.scale_log2, -lse2));
   } else if constexpr (MOD == MOD_REL_BIAS) {
     p = fast_exp2(__builtin_fmaf(__builtin_fmaf(sraw, a.scale, bias), kLog2e, -lse2));
-    return;
   } else if constexpr (MOD == MOD_ALIBI) {
-    x2 = (sraw * a.scale + slope * (float)(j - i)) * kLog2e;
+    p = fast_exp2(__builtin_fmaf(sraw, a.scale_log2, __builtin_fmaf(slope * kLog2e, (float)(j - i), -lse2)));
   } else if constexpr (MOD == MOD_SOFTCAP) {
-    const float th = tanh_exp2(sraw * a.scale * a.mod.inv_softcap);
-    x2 = a.mod.softcap * th * kLog2e;
-    grad = 1.0f - th * th;
+    const float r = fast_rcp(1.0f + fast_exp2(sraw * a.mod.softcap_k));
+    p = fast_exp2(__builtin_fmaf(r, a.mod.softcap_m, -0.5f * a.mod.softcap_m - lse2));
+    grad = 4.0f * __builtin_fmaf(-r, r, r);
   } else {
     int d = i - j;
     d = d < 0 ? -d : d;
     grad = d < a.mod.boost_radius ? a.mod.boost_factor : 1.0f;
-    x2 = sraw * a.scale * grad * kLog2e;
+    p = fast_exp2(__builtin_fmaf(sraw, a.scale_log2 * grad, -lse2));
   }
-  p = fast_exp2(x2 - lse2);
 }
 
 __device__ __forceinline__ u32x4 pack8(const f32x16& v, int base) {

@@ -219,30 +219,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
       // ---- softmax (as the bf16 kernel)
+      // Raw scores stay raw: masked pairs become -inf in place (the log2
+      // multiplier is > 0) and the multiplier folds into the exponent's FMA,
+      // one register flow for full and partial tiles.
       float mb = kNegInf;
-      if (cls == TILE_FULL) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mb = fmaxf(mb, st[t][r]);
-        mb = mb * a.scale_log2;
-      } else {
+      if (cls == TILE_PARTIAL) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int j = k0 + 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3);
-            float x = st[t][r] * a.scale_log2;
-            x = (j < Skv && mask_ok<MASK>(qi, j, window, 0, 0)) ? x : kNegInf;
-            st[t][r] = x;
-            mb = fmaxf(mb, x);
+            st[t][r] = (j < Skv && mask_ok<MASK>(qi, j, window, 0, 0)) ? st[t][r] : kNegInf;
           }
       }
-      mb = half_swap_max(mb);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mb = fmaxf(mb, st[t][r]);
+      mb = half_swap_max(mb * a.scale_log2);
       const float m_new = fmaxf(m, mb);
       const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
       const float alpha = fast_exp2(m - m_use);
-      const float mult = cls == TILE_FULL ? a.scale_log2 : 1.0f;
+      const float mult = a.scale_log2;
       float ps = 0.0f;
 #pragma unroll
       for (int t = 0; t < NT; ++t)
