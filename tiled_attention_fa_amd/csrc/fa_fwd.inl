@@ -332,6 +332,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int cls;
     if constexpr (BM) {
       cls = (k0 >= Skv) ? TILE_EMPTY : (st_c == TILE_FULL ? TILE_FULL : TILE_PARTIAL);
+      // A partial 128 x 128 tile is refined per wave and step with the
+      // analytic bounds of the mask: the wave's 32 x BN block may hold no
+      // admissible pair (above the diagonal, or below a window), or, for
+      // causal and window masks, only admissible pairs.  Document masks are
+      // causal within a document, so the causal bound applies to them too.
+      if constexpr (MASK != MASK_NONE) {
+        if (cls == TILE_PARTIAL) {
+          const int c2 = block_class<MASK == MASK_DOCUMENT ? MASK_CAUSAL : MASK>(qw0, 32, k0, BN, Skv, window);
+          if (c2 == TILE_EMPTY) cls = TILE_EMPTY;
+          if constexpr (MASK != MASK_DOCUMENT) {
+            if (c2 == TILE_FULL) cls = TILE_FULL;
+          }
+        }
+      }
     } else {
       cls = block_class<MASK>(qw0, 32, k0, BN, Skv, window);
     }
@@ -381,7 +395,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           const int ref = wave_uniform(doc_i);
           const bool keys_one = __builtin_amdgcn_ballot_w64(lane >= BN || ds[lane] == ref) == ~0ull;
           const bool rows_one = __builtin_amdgcn_ballot_w64(doc_i == ref) == ~0ull;
-          if (keys_one && rows_one) mode = 1;
+          // One document: only the causal test is left, and none at all
+          // when every key precedes every row of the wave.
+          if (keys_one && rows_one) mode = k0 + BN - 1 <= qw0 && k0 + BN <= Skv && qw0 + 31 < Sq ? 0 : 1;
         }
       } else if constexpr (MASK == MASK_CAUSAL) {
         mode = mode ? 1 : 0;
