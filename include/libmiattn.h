@@ -240,6 +240,23 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const uint8_t* q_
  * n_b must be B for FA_MASK_DOCUMENT and may be 1 otherwise).  One
  * stream-ordered pass; every entry of every array is written (unused list
  * slots are set to -1). */
+/* Bytes of one device allocation that holds every array of a block mask
+ * with n_b mask rows (1, or B for document masks) for sequence lengths Sq and
+ * Skv at 128 x 128 blocks, each array starting on a 256-byte boundary;
+ * with_orders adds q_order and kv_order.  block_q and block_kv must be 128.
+ * Returns 0 for invalid sizes (n_b < 1, lengths < 0 or too large, blocks
+ * other than 128). */
+size_t fa_block_mask_bytes(int n_b, int Sq, int Skv, int block_q, int block_kv, int with_orders);
+
+/* Fill *out (block sizes, counts and every array pointer) for a block mask
+ * carved from `base`, an allocation of at least fa_block_mask_bytes(...)
+ * bytes, 256-byte aligned, in the order tile_state, kv_count, kv_index,
+ * q_count, q_index[, q_order, kv_order].  Host only: no device access, no
+ * HIP call.  Returns FA_ERR_NULL, FA_ERR_ALIGN or FA_ERR_SHAPE on bad
+ * arguments, else FA_OK. */
+int fa_block_mask_layout(void* base, int n_b, int Sq, int Skv, int block_q, int block_kv, int with_orders,
+                         fa_block_mask* out);
+
 int fa_block_mask_build(int mask_kind, const fa_mask_params* mask_params,
                         int B, int Sq, int Skv, const fa_block_mask* out, void* stream);
 

@@ -205,3 +205,31 @@ def test_rel_bias_validation():
     op = fa.FaModParams(None, 0.0, 0, 1.0, None, 0x600000, 0x700000, need)
     assert fa.fa_bwd(P, P, P, P, P, P, P, P, P, P, 1 << 20, 1, 2, 2, 16, 16, 64, 0, 0.125, 0, None, 4,
                      ctypes.byref(op), None, None) == fa.FA_ERR_NULL
+
+
+def test_block_mask_bytes_and_layout():
+    """One allocation holds every block-mask array, each on a 256-byte boundary."""
+    L = fa.lib()
+    # S = 1000: 8 blocks; n_b = 2
+    parts = [2 * 8 * 8, 2 * 8 * 4, 2 * 8 * 8 * 4, 2 * 8 * 4, 2 * 8 * 8 * 4, 2 * 8 * 4, 2 * 8 * 4]
+    rnd = lambda n: (n + 255) // 256 * 256
+    assert fa.fa_block_mask_bytes(2, 1000, 1000, True) == sum(rnd(n) for n in parts)
+    assert fa.fa_block_mask_bytes(2, 1000, 1000, False) == sum(rnd(n) for n in parts[:5])
+    assert L.fa_block_mask_bytes(2, 1000, 1000, 64, 128, 1) == 0
+    assert L.fa_block_mask_bytes(0, 1000, 1000, 128, 128, 1) == 0
+    assert L.fa_block_mask_bytes(1, -1, 1000, 128, 128, 1) == 0
+    base = 0x10000000
+    s = fa.FaBlockMask()
+    assert L.fa_block_mask_layout(ctypes.c_void_p(base), 2, 1000, 1000, 128, 128, 1, ctypes.byref(s)) == fa.FA_OK
+    assert (s.block_q, s.block_kv, s.n_q, s.n_kv, s.n_b) == (128, 128, 8, 8, 2)
+    ptrs = [s.tile_state, s.kv_count, s.kv_index, s.q_count, s.q_index, s.q_order, s.kv_order]
+    off = 0
+    for p, n in zip(ptrs, parts):
+        assert p == base + off and p % 256 == 0
+        off += rnd(n)
+    s2 = fa.FaBlockMask()
+    assert L.fa_block_mask_layout(ctypes.c_void_p(base), 1, 300, 200, 128, 128, 0, ctypes.byref(s2)) == fa.FA_OK
+    assert s2.q_order is None and s2.kv_order is None and (s2.n_q, s2.n_kv) == (3, 2)
+    assert L.fa_block_mask_layout(None, 1, 300, 200, 128, 128, 0, ctypes.byref(s2)) == fa.FA_ERR_NULL
+    assert L.fa_block_mask_layout(ctypes.c_void_p(base + 16), 1, 300, 200, 128, 128, 0, ctypes.byref(s2)) == fa.FA_ERR_ALIGN
+    assert L.fa_block_mask_layout(ctypes.c_void_p(base), 1, 300, 200, 128, 64, 0, ctypes.byref(s2)) == fa.FA_ERR_SHAPE

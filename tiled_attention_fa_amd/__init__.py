@@ -12,7 +12,7 @@ from .binding import (  # noqa: F401
     TILE_EMPTY, TILE_PARTIAL, TILE_FULL, BLOCK, EXPORTED,
     FaMaskParams, FaModParams, FaBlockMask, FaError, BlockMask,
     lib, fa_fwd, fa_bwd, fa_bwd_phase, fa_block_mask_build, fa_bwd_workspace_bytes,
-    fa_bwd_rel_bias_workspace_bytes, fa_fwd_kv_step,
+    fa_bwd_rel_bias_workspace_bytes, fa_block_mask_bytes, fa_fwd_kv_step,
     fa_status_str, fa_version, default_scale, build_block_mask, forward, backward,
     FP8_BLOCK, quantize_fp8, forward_fp8,
 )

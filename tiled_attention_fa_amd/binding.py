@@ -28,7 +28,8 @@ FA_BWD_DELTA, FA_BWD_DKDV, FA_BWD_DQ = 1, 2, 4
 
 EXPORTED = ("fa_fwd", "fa_fwd_kv_step", "fa_bwd", "fa_bwd_phase", "fa_bwd_workspace_bytes",
             "fa_bwd_rel_bias_workspace_bytes",
-            "fa_block_mask_build", "fa_fp8_quantize", "fa_fwd_fp8", "fa_status_str", "fa_version")
+            "fa_block_mask_bytes", "fa_block_mask_layout", "fa_block_mask_build", "fa_fp8_quantize", "fa_fwd_fp8",
+            "fa_status_str", "fa_version")
 
 
 class FaMaskParams(ctypes.Structure):
@@ -84,6 +85,10 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.fa_bwd_rel_bias_workspace_bytes.argtypes = [_I, _I, _I, _I]
         L.fa_bwd_rel_bias_workspace_bytes.restype = ctypes.c_size_t
+        L.fa_block_mask_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
+        L.fa_block_mask_bytes.restype = ctypes.c_size_t
+        L.fa_block_mask_layout.argtypes = [_P, _I, _I, _I, _I, _I, _I, ctypes.POINTER(FaBlockMask)]
+        L.fa_block_mask_layout.restype = _I
         L.fa_block_mask_build.argtypes = [_I, ctypes.POINTER(FaMaskParams), _I, _I, _I,
                                           ctypes.POINTER(FaBlockMask), _P]
         L.fa_block_mask_build.restype = _I
@@ -222,20 +227,45 @@ def forward_fp8(q8, k8, v8, q_scale, k_scale, v_scale, *, scale=None, mask=MASK_
     return (out, lse) if return_lse else out
 
 
+def fa_block_mask_bytes(n_b: int, Sq: int, Skv: int, with_orders: bool = True) -> int:
+    return int(lib().fa_block_mask_bytes(n_b, Sq, Skv, BLOCK, BLOCK, int(with_orders)))
+
+
 class BlockMask:
-    """Device arrays of a 128 x 128 block mask (owned by torch tensors)."""
+    """Device arrays of a 128 x 128 block mask, carved from one allocation
+    by fa_block_mask_layout; the attributes are torch views of it."""
 
     def __init__(self, n_b, n_q, n_kv, device, orders=True):
         torch = _torch()
         self.n_b, self.n_q, self.n_kv = n_b, n_q, n_kv
-        self.tile_state = torch.empty((n_b, n_q, n_kv), dtype=torch.uint8, device=device)
-        self.kv_count = torch.empty((n_b, n_q), dtype=torch.int32, device=device)
-        self.kv_index = torch.empty((n_b, n_q, max(n_kv, 1)), dtype=torch.int32, device=device)
-        self.q_count = torch.empty((n_b, n_kv), dtype=torch.int32, device=device)
-        self.q_index = torch.empty((n_b, max(n_kv, 1), max(n_q, 1)), dtype=torch.int32, device=device)
+        Sq, Skv = n_q * BLOCK, n_kv * BLOCK
+        nbytes = fa_block_mask_bytes(n_b, Sq, Skv, orders)
+        if nbytes == 0:
+            raise FaError(FA_ERR_SHAPE, "fa_block_mask_bytes")
+        self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        s = FaBlockMask()
+        rc = lib().fa_block_mask_layout(ctypes.c_void_p(self.buffer.data_ptr()), n_b, Sq, Skv, BLOCK, BLOCK,
+                                        int(orders), ctypes.byref(s))
+        if rc != FA_OK:
+            raise FaError(rc, "fa_block_mask_layout")
+        base = self.buffer.data_ptr()
+
+        def view(addr, count, dtype, shape):
+            if addr is None:
+                return None
+            o = addr - base
+            n = count * (4 if dtype == torch.int32 else 1)
+            return self.buffer[o:o + n].view(dtype).view(shape)
+
+        nq1, nkv1 = max(n_q, 1), max(n_kv, 1)
+        self.tile_state = view(s.tile_state, n_b * n_q * n_kv, torch.uint8, (n_b, n_q, n_kv))
+        self.kv_count = view(s.kv_count, n_b * n_q, torch.int32, (n_b, n_q))
+        self.kv_index = view(s.kv_index, n_b * n_q * nkv1, torch.int32, (n_b, n_q, nkv1))
+        self.q_count = view(s.q_count, n_b * n_kv, torch.int32, (n_b, n_kv))
+        self.q_index = view(s.q_index, n_b * nkv1 * nq1, torch.int32, (n_b, nkv1, nq1))
         # longest-first tile orders (optional in the C struct)
-        self.q_order = torch.empty((n_b, max(n_q, 1)), dtype=torch.int32, device=device) if orders else None
-        self.kv_order = torch.empty((n_b, max(n_kv, 1)), dtype=torch.int32, device=device) if orders else None
+        self.q_order = view(s.q_order, n_b * nq1, torch.int32, (n_b, nq1)) if orders else None
+        self.kv_order = view(s.kv_order, n_b * nkv1, torch.int32, (n_b, nkv1)) if orders else None
 
     def struct(self) -> FaBlockMask:
         ptr = lambda t: None if t is None else t.data_ptr()

@@ -341,6 +341,62 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const v
                       mod_params, block_mask, stream);
 }
 
+// Sizes of the block-mask arrays in fa_block_mask_layout's order; false for
+// invalid arguments.
+static bool block_mask_parts(int n_b, int Sq, int Skv, int block_q, int block_kv, int with_orders, size_t (&part)[7],
+                             int& n_parts) {
+  if (block_q != kMaskBlock || block_kv != kMaskBlock) return false;
+  if (n_b < 1 || n_b > 65535 || Sq < 0 || Skv < 0 || Sq > kMaxSeq || Skv > kMaxSeq) return false;
+  const size_t nb = (size_t)n_b, nq = (size_t)cdiv(Sq, kMaskBlock), nkv = (size_t)cdiv(Skv, kMaskBlock);
+  const size_t nq1 = nq > 0 ? nq : 1, nkv1 = nkv > 0 ? nkv : 1;
+  part[0] = nb * nq * nkv;                    // tile_state, u8
+  part[1] = nb * nq * 4;                      // kv_count
+  part[2] = nb * nq * nkv1 * 4;               // kv_index
+  part[3] = nb * nkv * 4;                     // q_count
+  part[4] = nb * nkv1 * nq1 * 4;              // q_index
+  part[5] = with_orders ? nb * nq1 * 4 : 0;   // q_order
+  part[6] = with_orders ? nb * nkv1 * 4 : 0;  // kv_order
+  n_parts = with_orders ? 7 : 5;
+  return true;
+}
+
+size_t fa_block_mask_bytes(int n_b, int Sq, int Skv, int block_q, int block_kv, int with_orders) {
+  size_t part[7];
+  int n;
+  if (!block_mask_parts(n_b, Sq, Skv, block_q, block_kv, with_orders, part, n)) return 0;
+  size_t total = 0;
+  for (int i = 0; i < n; ++i) total += (part[i] + 255) & ~(size_t)255;
+  return total > 0 ? total : 256;
+}
+
+int fa_block_mask_layout(void* base, int n_b, int Sq, int Skv, int block_q, int block_kv, int with_orders,
+                         fa_block_mask* out) {
+  if (!base || !out) return FA_ERR_NULL;
+  if (!aligned(base, 256)) return FA_ERR_ALIGN;
+  size_t part[7];
+  int n;
+  if (!block_mask_parts(n_b, Sq, Skv, block_q, block_kv, with_orders, part, n)) return FA_ERR_SHAPE;
+  void* p[7] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  char* c = static_cast<char*>(base);
+  for (int i = 0; i < n; ++i) {
+    p[i] = c;
+    c += (part[i] + 255) & ~(size_t)255;
+  }
+  out->block_q = block_q;
+  out->block_kv = block_kv;
+  out->n_q = (int)cdiv(Sq, kMaskBlock);
+  out->n_kv = (int)cdiv(Skv, kMaskBlock);
+  out->n_b = n_b;
+  out->tile_state = static_cast<uint8_t*>(p[0]);
+  out->kv_count = static_cast<int32_t*>(p[1]);
+  out->kv_index = static_cast<int32_t*>(p[2]);
+  out->q_count = static_cast<int32_t*>(p[3]);
+  out->q_index = static_cast<int32_t*>(p[4]);
+  out->q_order = static_cast<int32_t*>(p[5]);
+  out->kv_order = static_cast<int32_t*>(p[6]);
+  return FA_OK;
+}
+
 int fa_block_mask_build(int mask_kind, const fa_mask_params* mask_params, int B, int Sq, int Skv,
                         const fa_block_mask* out, void* stream) {
   if (!out) return FA_ERR_NULL;
