@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -44,17 +45,23 @@ def source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when there is none for this kernel or the sources changed since."""
+def measured_profile(workload: str, kernel: str) -> dict:
+    """The committed rocprofv3 figures of one kernel (HBM bytes per launch,
+    average shader clock), or {} when there are none for this kernel or the
+    sources changed since they were taken."""
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
-        return None
+        return {}
     rec = json.load(open(p))
     k = rec.get("kernels", {}).get(kernel)
     if not k or rec.get("source_sha") != source_sha():
-        return None
-    return k.get("bytes_per_launch")
+        return {}
+    return k
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed counter summary, or None."""
+    return measured_profile(workload, kernel).get("bytes_per_launch")
 
 
 def cpu_baseline(w, heads: int):
@@ -233,7 +240,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(end) / args.steps
-    kernel_ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, n in enumerate(names)}
+    per_step = {n: sorted(e[i].elapsed_time(e[i + 1]) for e in evs) for i, n in enumerate(names)}
+    kernel_ms = {n: sum(t) / args.steps for n, t in per_step.items()}
 
     npairs = flops.pairs(w.mask, w.B, w.Hq, w.S, w.S, w.window, extras.get("doc_lengths"))
     f_fwd = flops.fwd_flops(npairs, w.D)
@@ -270,11 +278,19 @@ def main():
         "bwd_tflops": round(f_bwd / (sum(kernel_ms[n] for n in names if n.startswith("bwd")) * 1e-3) / 1e12, 2)
         if w.backward else None,
         "kernel_ms": {n: round(t, 4) for n, t in kernel_ms.items()},
+        "kernel_ms_median": {n: round(statistics.median(t), 4) for n, t in per_step.items()},
+        "kernel_ms_min": {n: round(t[0], 4) for n, t in per_step.items()},
         "wall_s": round(wall, 3),
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(w.name, dominant)},
     }
+    # The peak scaled to the shader clock the profiler saw under this kernel
+    # (busy cycles over duration); the nominal peak assumes 2.4 GHz.
+    ghz = measured_profile(w.name, dominant).get("clock_ghz")
+    rec["clock"] = None if ghz is None else {
+        "kernel": dominant, "ghz": round(ghz, 3), "peak_at_clock": round(peak * ghz / 2.4, 1),
+        "frac_at_clock": round(achieved / (peak * ghz / 2.4), 4)}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
     print(json.dumps(rec), flush=True)
