@@ -9,6 +9,8 @@ Recipe (fixed, so every run sees the same bits):
   * Q, K, V, dO are float32 N(0, 1) drawn from a CPU ``torch.Generator``
     seeded with ``seed``, then rounded to bfloat16 with round-to-nearest-even
     (``Tensor.to(torch.bfloat16)``).  The fp32 workload keeps float32.
+  * Tensors too large to draw at once (``randn_chunked``) are filled in
+    chunks of 2^24 values, each from its own seeded generator.
   * Document lengths are integers drawn uniformly from [lo, hi] inclusive with
     ``numpy.random.default_rng(seed)`` until their sum reaches the packed
     length; the last one is cut so the sum is exact.
@@ -32,6 +34,20 @@ def randn(shape, seed: int, dtype: str = "bf16") -> torch.Tensor:
     g.manual_seed(int(seed))
     x = torch.randn(*shape, generator=g, dtype=torch.float32)
     return x.to(_DTYPES[dtype]).contiguous()
+
+
+def randn_chunked(shape, seed: int, dtype: str = "bf16", chunk: int = 1 << 24) -> torch.Tensor:
+    """Like ``randn`` for very large tensors: the flattened tensor is filled
+    in chunks of ``chunk`` values, chunk c drawn from a CPU generator seeded
+    with ``seed * 1000003 + c``, so no float32 copy of the whole tensor is
+    ever held.  (Different values from ``randn`` with the same seed.)"""
+    out = torch.empty(int(np.prod(shape)), dtype=_DTYPES[dtype])
+    g = torch.Generator(device="cpu")
+    for c, lo in enumerate(range(0, out.numel(), chunk)):
+        n = min(chunk, out.numel() - lo)
+        g.manual_seed(int(seed) * 1000003 + c)
+        out[lo:lo + n] = torch.randn(n, generator=g, dtype=torch.float32).to(_DTYPES[dtype])
+    return out.view(*shape)
 
 
 def qkv(B, Hq, Hkv, Sq, Skv, D, seed: int, dtype: str = "bf16"):

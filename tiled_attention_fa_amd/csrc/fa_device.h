@@ -276,6 +276,20 @@ __device__ __forceinline__ void decode_work(int P, int B, int Hq, int Hkv, int n
   tile = heavy_first ? (n_tiles - 1 - r) : r;
 }
 
+// Running row sum with compensation (Kahan): l is the sum, c the negated
+// low-order part lost so far, so the sum is l - c.  After every key step,
+// l <- alpha l + ps with ps the step's sum.  Over 10^5 steps of nearly equal
+// step sums (millions of keys with one score) a plain fp32 sum drifts by up
+// to ~1e-3 relative; the compensated one stays at rounding level.
+__device__ __forceinline__ void row_sum_update(float& l, float& c, float alpha, float ps) {
+  const float ls = l * alpha;
+  c *= alpha;
+  const float y = ps - c;
+  const float t = ls + y;
+  c = (t - ls) - y;
+  l = t;
+}
+
 // Tile at position r of a block mask's longest-first order, or `fallback`
 // when the mask carries no order.  The entry is clamped into [0, n).
 __device__ __forceinline__ int ordered_tile(const int32_t* order, int n_b, int b, int n, int r, int fallback) {

@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     tile_load8<D, BN>(rows_rsrc(V, Skv, k0, D), vs, wave, lane);
   };
 
-  float m = kNegInf, l = 0.0f;
+  float m = kNegInf, l = 0.0f, lc = 0.0f;  // lc: compensation of l
   f32x16 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           st[t][r] = p;
           ps += p;
         }
-      l = l * alpha + ps;
+      row_sum_update(l, lc, alpha, ps);
       m = m_new;
       if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (s + 1 < n_steps) step(s + 1, sK1, sV1, sK0, sV0);
   }
 
-  const float lt = half_swap_sum(l);
+  const float lt = half_swap_sum(l - lc);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (row_ok) {
     uint16_t* Orow = (uint16_t*)a.o + ((size_t)(b * a.Hq + hq) * Sq + qi) * D;

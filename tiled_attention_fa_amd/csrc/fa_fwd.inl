@@ -309,6 +309,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   float m = kNegInf, l = 0.0f;  // m: running max in log2 units; l: this lane's partial sum
+  float lc = 0.0f;              // compensation of l
   f32x16 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
@@ -425,7 +426,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           st[t][r] = p;
           ps += p;
         }
-      l = l * alpha + ps;
+      row_sum_update(l, lc, alpha, ps);
       m = m_new;
       if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
@@ -518,7 +519,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // ---- epilogue: O = acc / l, LSE = ln 2 (m + log2 l) (+ the constant the
   // softcap form leaves out)
-  const float lt = half_swap_sum(l);
+  const float lt = half_swap_sum(l - lc);
   const float lse_shift = MOD == MOD_SOFTCAP ? a.mod.softcap : 0.0f;
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (row_ok) {
@@ -623,6 +624,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   float m = kNegInf, l = 0.0f;  // running max (log2 units), this lane's partial row sum
+  float lc = 0.0f;              // compensation of l
   f32x16 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
@@ -704,7 +706,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         st[t][r] = p;
         ps += p;
       }
-    l = l * alpha + ps;
+    row_sum_update(l, lc, alpha, ps);
     m = m_new;
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
@@ -754,7 +756,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // ---- epilogue: O = acc / l, LSE = ln 2 (m + log2 l) (+ the constant the
   // softcap form leaves out)
-  const float lt = half_swap_sum(l);
+  const float lt = half_swap_sum(l - lc);
   const float lse_shift = MOD == MOD_SOFTCAP ? a.mod.softcap : 0.0f;
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (row_ok) {
