@@ -10,7 +10,7 @@ hold at any length (the oracle's dense rows are too slow at millions of keys).
       Z     = sum_R e^(s_j - m) + z_i e^(-m),     LSE_i = m + ln Z.
   A key or value read from the wrong row moves a random key's weight onto
   another value and fails the check.
-* Forward and backward at 262,144 tokens with identical keys.  Every score
+* Forward and backward at 262,144 and 4,194,304 tokens with identical keys.  Every score
   of row i is the same number c_i = scale q_i . k, so under the causal mask
   P_ij = 1/(i+1) for j <= i and:
       O_i   = mean of V_0..V_i,       LSE_i = c_i + ln(i + 1),
@@ -96,8 +96,9 @@ def _suffix_at(sorted_js, S, seg_sum):
     return out
 
 
-def test_identical_keys_forward_backward_long():
-    S, D = 1 << 18, 128
+@pytest.mark.parametrize("S", [1 << 18, MAX_SEQ])
+def test_identical_keys_forward_backward_long(S):
+    D = 128
     scale = f32_scale(D)
     q = synth.randn_chunked((1, 1, S, D), 777)
     v = synth.randn_chunked((1, 1, S, D), 778)
