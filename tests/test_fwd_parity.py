@@ -192,3 +192,20 @@ def test_long_window(spec):
     (o, lse), o_ref, l_ref = run_case(1, 2, 1, 2600, 2600, 128, "bf16", spec, seed=31)
     check_out(o, o_ref, "bf16")
     check_lse(lse, l_ref)
+
+
+@pytest.mark.parametrize("mask", [0, 1])
+def test_softcap_mixed_forms(mask):
+    """Key blocks of alternating scale (x1, x8): in the x8 blocks most scores
+    saturate the cap (|s| >> c), in the x1 blocks none do, so every row mixes
+    steps far out on both tails of tanh with steps near its linear part."""
+    B, H, S, D = 1, 4, 700, 128
+    q, k, v = synth.qkv(B, H, H, S, S, D, 31)
+    f = torch.where((torch.arange(S) // 64) % 2 == 0, 1.0, 8.0)[None, None, :, None]
+    k = (k.float() * f).to(torch.bfloat16)
+    spec = dict(mask=mask, mod=2, softcap=30.0)
+    o, lse = fa.forward(dev(q), dev(k), dev(v), return_lse=True, **spec)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.forward(q, k, v, f32_scale(D), oracle.Variant(**spec))
+    check_out(o, o_ref, "bf16")
+    check_lse(lse, l_ref)
