@@ -94,6 +94,9 @@ def test_fwd_rejects_bad_params():
     assert fwd(mod=2) == fa.FA_ERR_NULL
     assert fwd(mod=2, op=fa.FaModParams(None, 0.0, 0, 1.0)) == fa.FA_ERR_PARAM
     assert fwd(mod=2, op=fa.FaModParams(None, float("inf"), 0, 1.0)) == fa.FA_ERR_PARAM
+    # scale log2(e) and 2 scale log2(e) / softcap must be finite in fp32
+    assert fwd(scale=3.0e38) == fa.FA_ERR_PARAM
+    assert fwd(mod=2, op=fa.FaModParams(None, 1e-40, 0, 1.0)) == fa.FA_ERR_PARAM
     assert fwd(mod=3, op=fa.FaModParams(None, 0.0, -1, 1.1)) == fa.FA_ERR_PARAM
     assert fwd(mod=3, op=fa.FaModParams(None, 0.0, 5, float("nan"))) == fa.FA_ERR_PARAM
     assert fwd(mod=8) == fa.FA_ERR_UNSUPPORTED

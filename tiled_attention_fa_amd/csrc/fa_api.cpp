@@ -43,7 +43,8 @@ float log2_multiplier(float scale) {
 // modifier argument blocks.
 int check_variant(int B, int Hq, int Sq, int Skv, float scale, int mask_kind, const fa_mask_params* mp,
                   int mod_kind, const fa_mod_params* op, MaskArgs& mask, ModArgs& mod) {
-  if (!std::isfinite(scale) || scale < 0.0f) return FA_ERR_PARAM;
+  // The kernels multiply raw scores by scale log2(e), which must stay finite.
+  if (!std::isfinite(scale) || scale < 0.0f || !std::isfinite(log2_multiplier(scale))) return FA_ERR_PARAM;
   mask = MaskArgs{0, nullptr};
   mod = ModArgs{nullptr, 1.0f, 1.0f, 0, 1.0f, nullptr, nullptr, nullptr, 0.0f, -1.0f};
   switch (mask_kind) {
@@ -77,6 +78,7 @@ int check_variant(int B, int Hq, int Sq, int Skv, float scale, int mask_kind, co
       mod.inv_softcap = 1.0f / op->softcap;
       mod.softcap_k = (float)(2.0 * (double)scale * 1.4426950408889634 / (double)op->softcap);
       mod.softcap_m = (float)(-2.0 * (double)op->softcap * 1.4426950408889634);
+      if (!std::isfinite(mod.softcap_k) || !std::isfinite(mod.softcap_m)) return FA_ERR_PARAM;
       break;
     case FA_MOD_LOCAL_BOOST:
       if (!op) return FA_ERR_NULL;
