@@ -143,7 +143,9 @@ typedef struct {
 
 /* Forward pass.  q, k, v, out: device, dtype elements in the layout above.
  * lse: device float [B][Hq][Sq] or NULL (no LSE written).  scale multiplies
- * q . k before the modifier.  mask_params / mod_params: host structs, may be
+ * q . k before the modifier; it must be finite and >= 0 with scale * log2(e)
+ * finite in fp32 (and 2 scale log2(e) / softcap for FA_MOD_SOFTCAP), else
+ * FA_ERR_PARAM.  mask_params / mod_params: host structs, may be
  * NULL when the kind needs no parameter.  block_mask: NULL (tile ranges
  * derived from the mask kind) or a mask built for this (mask, B, Sq, Skv);
  * when given, only its non-empty tiles are visited and FULL tiles skip the
