@@ -82,6 +82,17 @@ def test_sq_ne_skv(Sq, Skv, mask, D):
     check_lse(lse, l_ref)
 
 
+@pytest.mark.parametrize("Sq,Skv", [(200, 333), (333, 200), (700, 64)])
+@pytest.mark.parametrize("name", ["window", "causal_alibi", "softcap", "boost", "window_boost"])
+@pytest.mark.parametrize("D,dtype", [(64, "f32"), (128, "bf16")])
+def test_sq_ne_skv_modifiers(Sq, Skv, name, D, dtype):
+    """Unequal lengths with every modifier and the window (absolute indices;
+    with the window and Sq > Skv + window - 1 the last rows have no key)."""
+    (o, lse), o_ref, l_ref = run_case(1, 4, 2, Sq, Skv, D, dtype, VARIANTS[name], seed=Sq * 3 + Skv)
+    check_out(o, o_ref, dtype)
+    check_lse(lse, l_ref)
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 4), (8, 2), (8, 1)])
 def test_gqa_ratios(Hq, Hkv):
     (o, lse), o_ref, l_ref = run_case(2, Hq, Hkv, 260, 260, 128, "bf16", dict(mask=1, mod=1), seed=Hq * 10 + Hkv)
