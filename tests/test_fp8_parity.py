@@ -95,6 +95,32 @@ def test_fp8_forward_matches_oracle(mask, window, D):
     check_lse(lse.view(B * Hq, S), L)
 
 
+@pytest.mark.parametrize("Sq,Skv", [(200, 333), (333, 200), (700, 64)])
+@pytest.mark.parametrize("mask,window", [(0, 0), (1, 0), (2, 90)])
+def test_fp8_sq_ne_skv(Sq, Skv, mask, window):
+    """Unequal query and key lengths (absolute indices; with the window and
+    Sq > Skv + window - 1 the last rows have no key: O = 0, LSE = -inf)."""
+    B, Hq, Hkv, D = 1, 4, 2, 128
+    s = synth.signs(D, 83).numpy()
+    q, _, _ = synth.qkv(B, Hq, Hkv, Sq, Sq, D, 84)
+    _, k, v = synth.qkv(B, Hq, Hkv, Skv, Skv, D, 85)
+    q8, qs = ofp8.block_quantize(_f64(q).reshape(B * Hq, Sq, D), s)
+    k8, ks = ofp8.block_quantize(_f64(k).reshape(B * Hkv, Skv, D), s)
+    v8, vs = ofp8.block_quantize(_f64(v).reshape(B * Hkv, Skv, D))
+
+    def gpu(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    o, lse = fa.forward_fp8(gpu(q8).view(B, Hq, Sq, D), gpu(k8).view(B, Hkv, Skv, D), gpu(v8).view(B, Hkv, Skv, D),
+                            gpu(qs), gpu(ks), gpu(vs), scale=f32_scale(D), mask=mask, window=window,
+                            return_lse=True)
+    torch.cuda.synchronize()
+    O, L = ofp8.fp8_forward(q8, k8, v8, qs, ks, vs, f32_scale(D), oracle.Variant(mask=mask, window=window),
+                            Hq=Hq, Hkv=Hkv)
+    _check_fp8_out(o.cpu().view(B * Hq, Sq, D), O, np.abs(ofp8.dequantize(v8, vs)).max())
+    check_lse(lse.cpu().view(B * Hq, Sq), L)
+
+
 def test_fp8_workload_sampled_rows():
     """The FP8 benchmark workload at full size (B2 H16 S8192 D128 causal) on
     256 sampled rows of every head."""
