@@ -121,3 +121,26 @@ def test_sq_ne_skv(Sq, Skv, name, D):
     for g, r, what in zip((dq, dk, dv), (rq, rk, rv), ("dQ", "dK", "dV")):
         bar = MAX_EXCESS_LENGTHS.get((Sq, Skv, name))
         check_out(g, r, "bf16", what, max_excess=bar, rounding_mean=bar is not None)
+
+
+@pytest.mark.parametrize("Sq,Skv", [(300, 520), (520, 300)])
+@pytest.mark.parametrize("name", ["none", "causal", "window"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_block_mask_unequal_lengths(Sq, Skv, name, D):
+    """Forward and backward through a block mask built for Sq != Skv, GQA."""
+    spec = LENGTH_SPECS[name]
+    q, _, _ = synth.qkv(1, 4, 2, Sq, Sq, D, 50)
+    _, k, v = synth.qkv(1, 4, 2, Skv, Skv, D, 51)
+    do = synth.randn((1, 4, Sq, D), 52)
+    scale = f32_scale(D)
+    bm = fa.build_block_mask(spec["mask"], 1, Sq, Skv, window=spec.get("window", 0))
+    qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
+    o, lse = fa.forward(qd, kd, vd, scale=scale, return_lse=True, block_mask=bm, **spec)
+    dq, dk, dv = fa.backward(qd, kd, vd, o, dod, lse, scale=scale, block_mask=bm, **spec)
+    torch.cuda.synchronize()
+    var = oracle.Variant(**spec)
+    o_ref, _ = oracle.forward(q, k, v, scale, var)
+    rq, rk, rv = oracle.backward(q, k, v, do, scale, var)
+    check_out(o, o_ref, "bf16", "O")
+    for g, r, what in zip((dq, dk, dv), (rq, rk, rv), ("dQ", "dK", "dV")):
+        check_out(g, r, "bf16", what)
