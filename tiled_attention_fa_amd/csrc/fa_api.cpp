@@ -46,7 +46,7 @@ int check_variant(int B, int Hq, int Sq, int Skv, float scale, int mask_kind, co
   // The kernels multiply raw scores by scale log2(e), which must stay finite.
   if (!std::isfinite(scale) || scale < 0.0f || !std::isfinite(log2_multiplier(scale))) return FA_ERR_PARAM;
   mask = MaskArgs{0, nullptr};
-  mod = ModArgs{nullptr, 1.0f, 1.0f, 0, 1.0f, nullptr, nullptr, nullptr, 0.0f, -1.0f};
+  mod = ModArgs{nullptr, 1.0f, 0, 1.0f, nullptr, nullptr, nullptr, 0.0f, -1.0f};
   switch (mask_kind) {
     case FA_MASK_NONE:
     case FA_MASK_CAUSAL: break;
@@ -75,7 +75,6 @@ int check_variant(int B, int Hq, int Sq, int Skv, float scale, int mask_kind, co
       if (!op) return FA_ERR_NULL;
       if (!std::isfinite(op->softcap) || !(op->softcap > 0.0f)) return FA_ERR_PARAM;
       mod.softcap = op->softcap;
-      mod.inv_softcap = 1.0f / op->softcap;
       mod.softcap_k = (float)(2.0 * (double)scale * 1.4426950408889634 / (double)op->softcap);
       mod.softcap_m = (float)(-2.0 * (double)op->softcap * 1.4426950408889634);
       if (!std::isfinite(mod.softcap_k) || !std::isfinite(mod.softcap_m)) return FA_ERR_PARAM;

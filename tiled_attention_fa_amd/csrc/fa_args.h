@@ -20,7 +20,7 @@ struct MaskArgs {
 
 struct ModArgs {
   const float* slopes;  // [Hq] or null: 2^(-8(h+1)/Hq)
-  float softcap, inv_softcap;
+  float softcap;
   int boost_radius;
   float boost_factor;
   // Relative-position bias: s + rel_bias[h][i - j + Skv - 1], [Hq][Sq + Skv - 1].

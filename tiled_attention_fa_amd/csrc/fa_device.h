@@ -217,35 +217,6 @@ __device__ __forceinline__ float head_slope(const ModArgs& m, int h, int Hq) {
   return 0.0f;
 }
 
-// tanh from exp2: tanh(x) = 1 - 2 / (1 + 2^(2x log2 e)).
-__device__ __forceinline__ float tanh_exp2(float x) {
-  const float e = fast_exp2(2.0f * kLog2e * x);
-  return 1.0f - 2.0f * fast_rcp(1.0f + e);
-}
-
-// Modified score from the scaled score s, query i, key j.
-template <int MOD>
-__device__ __forceinline__ float apply_mod(float s, int i, int j, float slope, const ModArgs& m) {
-  if constexpr (MOD == MOD_NONE) return s;
-  if constexpr (MOD == MOD_ALIBI) return s + slope * (float)(j - i);
-  if constexpr (MOD == MOD_SOFTCAP) return m.softcap * tanh_exp2(s * m.inv_softcap);
-  int d = i - j;
-  d = d < 0 ? -d : d;
-  return d < m.boost_radius ? s * m.boost_factor : s;
-}
-
-// d(modified)/ds for the backward pass; `t` is tanh(s / softcap) for MOD_SOFTCAP.
-template <int MOD>
-__device__ __forceinline__ float mod_grad(int i, int j, float t, const ModArgs& m) {
-  if constexpr (MOD == MOD_SOFTCAP) return 1.0f - t * t;
-  if constexpr (MOD == MOD_BOOST) {
-    int d = i - j;
-    d = d < 0 ? -d : d;
-    return d < m.boost_radius ? m.boost_factor : 1.0f;
-  }
-  return 1.0f;
-}
-
 // ---------------------------------------------------------------- schedule
 // Workgroups are handed to the 8 XCDs round-robin by id.  When the number
 // of (batch, kv-head) units is a multiple of 8, every unit is pinned to one
