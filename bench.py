@@ -151,7 +151,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        print("bench.py: the library runs on one GPU (no multi-GPU path); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
