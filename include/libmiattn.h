@@ -198,7 +198,8 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq, int D);
 /* Size of the scratch a relative-bias gradient needs (fa_mod_params
  * rel_bias_ws): one float row of Skv + 128 per (batch, query head, 128-row
  * query tile), the per-tile diagonal sums that a fixed-order reduction then
- * adds up.  0 when any size is 0. */
+ * adds up.  It grows as B Hq Sq Skv / 32 bytes: 68 MB at B=2, Hq=16,
+ * Sq=Skv=8192; 2.2 GB at B=1, Hq=16, Sq=Skv=65536.  0 when any size is 0. */
 size_t fa_bwd_rel_bias_workspace_bytes(int B, int Hq, int Sq, int Skv);
 
 /* FP8 path ("FlashAttention-3 (KO)" page, technical innovation 3: FP8
