@@ -109,6 +109,15 @@ def test_block_mask_path(name):
     check_lse(lse, l_ref)
 
 
+@pytest.mark.parametrize("name", ["causal", "document", "window_boost"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_block_mask_path_f32(name, D):
+    """fp32 inputs through the block-mask path (fp32 products, 32-key steps)."""
+    (o, lse), o_ref, l_ref = run_case(1, 2, 2, 450, 450, D, "f32", VARIANTS[name], seed=6, block_mask=True)
+    check_out(o, o_ref, "f32")
+    check_lse(lse, l_ref)
+
+
 def test_lse_does_not_change_output():
     """Writing the LSE must not change O: same arithmetic, bit-identical."""
     q, k, v = (dev(t) for t in synth.qkv(2, 4, 2, 300, 300, 128, 3))
