@@ -94,9 +94,10 @@ def test_sq_ne_skv_modifiers(Sq, Skv, name, D, dtype):
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 4), (8, 2), (8, 1)])
-def test_gqa_ratios(Hq, Hkv):
-    (o, lse), o_ref, l_ref = run_case(2, Hq, Hkv, 260, 260, 128, "bf16", dict(mask=1, mod=1), seed=Hq * 10 + Hkv)
-    check_out(o, o_ref, "bf16")
+@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "f32")])
+def test_gqa_ratios(Hq, Hkv, D, dtype):
+    (o, lse), o_ref, l_ref = run_case(2, Hq, Hkv, 260, 260, D, dtype, dict(mask=1, mod=1), seed=Hq * 10 + Hkv)
+    check_out(o, o_ref, dtype)
     check_lse(lse, l_ref)
 
 
