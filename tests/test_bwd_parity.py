@@ -62,8 +62,9 @@ def test_lengths_causal(S):
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (4, 2), (4, 1)])
-def test_gqa_group_sums(Hq, Hkv):
-    got, ref = run_bwd(2, Hq, Hkv, 200, 128, dict(mask=1, mod=1), seed=7)
+@pytest.mark.parametrize("D", [64, 128])
+def test_gqa_group_sums(Hq, Hkv, D):
+    got, ref = run_bwd(2, Hq, Hkv, 200, D, dict(mask=1, mod=1), seed=7)
     for g, r, what in zip(got, ref, ("dQ", "dK", "dV")):
         check_out(g, r, "bf16", what)
 
