@@ -236,3 +236,25 @@ def test_block_mask_bytes_and_layout():
     assert L.fa_block_mask_layout(None, 1, 300, 200, 128, 128, 0, ctypes.byref(s2)) == fa.FA_ERR_NULL
     assert L.fa_block_mask_layout(ctypes.c_void_p(base + 16), 1, 300, 200, 128, 128, 0, ctypes.byref(s2)) == fa.FA_ERR_ALIGN
     assert L.fa_block_mask_layout(ctypes.c_void_p(base), 1, 300, 200, 128, 64, 0, ctypes.byref(s2)) == fa.FA_ERR_SHAPE
+
+
+def test_binding_rejects_strided_or_mismatched_tensors():
+    """The torch conveniences check layouts before calling the library: the C
+    ABI reads dense arrays, so a strided view or a mismatched tensor would be
+    read as the wrong elements (these checks run before any HIP call)."""
+    import pytest
+    import torch
+    q = torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="contiguous"):
+        fa.forward(q.transpose(2, 3).contiguous().transpose(2, 3), k, k)
+    with pytest.raises(ValueError, match="shape"):
+        fa.forward(q, torch.zeros(1, 2, 16, 128, dtype=torch.bfloat16), k)
+    with pytest.raises(ValueError, match="dtype"):
+        fa.forward(q, k, k.float())
+    with pytest.raises(ValueError, match="doc_ids"):
+        fa.forward(q, k, k, mask=fa.MASK_DOCUMENT, doc_ids=torch.zeros(1, 15, dtype=torch.int32))
+    with pytest.raises(ValueError, match="lse"):
+        fa.backward(q, k, k, q, q, torch.zeros(1, 2, 15))
+    with pytest.raises(ValueError, match="dk"):
+        fa.backward(q, k, k, q, q, torch.zeros(1, 2, 16), grads=(q, k[:, :1], k))

@@ -156,6 +156,43 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _dense(t, what, shape=None, dtypes=None, device=None):
+    """Check that ``t`` (if given) is a dense row-major tensor of ``shape``
+    (None entries are free) with a dtype in ``dtypes`` on ``device``; the C
+    ABI reads plain arrays from the data pointer, so a strided view or a
+    tensor of another shape would be read as the wrong elements."""
+    if t is None:
+        return None
+    if shape is not None and (t.dim() != len(shape) or
+                              any(w is not None and w != g for w, g in zip(shape, t.shape))):
+        raise ValueError(f"{what}: shape {tuple(t.shape)} does not match {tuple(shape)}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{what}: dtype {t.dtype} not in {tuple(dtypes)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{what}: on {t.device}, expected {device}")
+    return t
+
+
+def _check_qkv(q, k, v):
+    """Shapes (B, Hq, Hkv, Sq, Skv, D) of q [B,Hq,Sq,D], k and v [B,Hkv,Skv,D]."""
+    torch = _torch()
+    _dense(q, "q", (None, None, None, None), (torch.bfloat16, torch.float32))
+    B, Hq, Sq, D = q.shape
+    _dense(k, "k", (B, None, None, D), (q.dtype,), q.device)
+    Hkv, Skv = k.shape[1], k.shape[2]
+    _dense(v, "v", (B, Hkv, Skv, D), (q.dtype,), q.device)
+    return B, Hq, Hkv, Sq, Skv, D
+
+
+def _check_mod_tensors(q, Hq, Sq, Skv, doc_ids, alibi_slopes, rel_bias):
+    torch = _torch()
+    _dense(doc_ids, "doc_ids", (q.shape[0], Sq), (torch.int32,), q.device)
+    _dense(alibi_slopes, "alibi_slopes", (Hq,), (torch.float32,), q.device)
+    _dense(rel_bias, "rel_bias", (Hq, Sq + Skv - 1), (torch.float32,), q.device)
+
+
 def _stream(stream):
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -194,11 +231,17 @@ def quantize_fp8(x, signs=None, *, out=None, scales=None, stream=None):
     tensor; with ``signs`` (float32 [D] of +-1) the rows are first multiplied
     by diag(signs) H / sqrt(D) (incoherent processing)."""
     torch = _torch()
+    _dense(x, "x", (None, None, None, None), (torch.bfloat16,))
     B, H, S, D = x.shape
+    _dense(signs, "signs", (D,), (torch.float32,), x.device)
     if out is None:
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((B, H, -(-S // FP8_BLOCK)), dtype=torch.uint8, device=x.device)
+    _dense(out, "out", tuple(x.shape), (torch.uint8,), x.device)
+    _dense(scales, "scales", None, (torch.uint8,), x.device)
+    if scales.numel() < B * H * -(-S // FP8_BLOCK):
+        raise ValueError(f"scales: {scales.numel()} bytes, need {B * H * -(-S // FP8_BLOCK)}")
     rc = lib().fa_fp8_quantize(_ptr(x), _ptr(out), _ptr(scales), int(B * H), int(S), int(D), _ptr(signs),
                                _stream(stream))
     if rc != FA_OK:
@@ -211,12 +254,23 @@ def forward_fp8(q8, k8, v8, q_scale, k_scale, v_scale, *, scale=None, mask=MASK_
     """bf16 O (and LSE) from E4M3 q8 [B,Hq,Sq,D], k8/v8 [B,Hkv,Skv,D] with their
     block scales (masks: none, causal, sliding window)."""
     torch = _torch()
+    u8 = (torch.uint8,)
+    _dense(q8, "q8", (None, None, None, None), u8)
     B, Hq, Sq, D = q8.shape
+    _dense(k8, "k8", (B, None, None, D), u8, q8.device)
     Hkv, Skv = k8.shape[1], k8.shape[2]
+    _dense(v8, "v8", (B, Hkv, Skv, D), u8, q8.device)
+    for t, what, rows, n in ((q_scale, "q_scale", B * Hq, Sq), (k_scale, "k_scale", B * Hkv, Skv),
+                             (v_scale, "v_scale", B * Hkv, Skv)):
+        _dense(t, what, None, u8, q8.device)
+        if t is not None and t.numel() < rows * -(-n // FP8_BLOCK):
+            raise ValueError(f"{what}: {t.numel()} bytes, need {rows * -(-n // FP8_BLOCK)}")
     if out is None:
         out = torch.empty((B, Hq, Sq, D), dtype=torch.bfloat16, device=q8.device)
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q8.device)
+    _dense(out, "out", (B, Hq, Sq, D), (torch.bfloat16,), q8.device)
+    _dense(lse if return_lse else None, "lse", (B, Hq, Sq), (torch.float32,), q8.device)
     mp, _ = _params(mask, window, None, None, MOD_NONE, None, 0.0, 0, 1.0)
     sc = default_scale(D) if scale is None else float(scale)
     rc = lib().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(out),
@@ -280,6 +334,8 @@ def build_block_mask(mask: int, B: int, Sq: int, Skv: int, *, window: int = 0, d
     """Build (or rebuild ``into``, allocating nothing) the block mask of a mask kind;
     ``orders`` adds the longest-first tile orders the kernels schedule by."""
     n_b = B if mask == MASK_DOCUMENT else 1
+    if doc_ids is not None:
+        _dense(doc_ids, "doc_ids", (B, Sq), (_torch().int32,))
     bm = into if into is not None else BlockMask(n_b, -(-Sq // BLOCK), -(-Skv // BLOCK), device, orders)
     mp, _ = _params(mask, window, doc_ids, None, MOD_NONE, None, 0.0, 0, 1.0)
     s = bm.struct()
@@ -296,12 +352,15 @@ def forward(q, k, v, *, scale=None, mask=MASK_NONE, window=0, doc_ids=None, mod=
 
     ``rel_bias`` (MOD_REL_BIAS): float32 [Hq, Sq + Skv - 1] on the device."""
     torch = _torch()
-    B, Hq, Sq, D = q.shape
-    Hkv, Skv = k.shape[1], k.shape[2]
+    B, Hq, Hkv, Sq, Skv, D = _check_qkv(q, k, v)
+    _check_mod_tensors(q, Hq, Sq, Skv, doc_ids, alibi_slopes, rel_bias)
+    _dense(visited, "visited", None, (torch.int32,), q.device)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty((B, Hq, Sq, D), dtype=q.dtype, device=q.device)
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    _dense(out, "out", (B, Hq, Sq, D), (q.dtype,), q.device)
+    _dense(lse if return_lse else None, "lse", (B, Hq, Sq), (torch.float32,), q.device)
     mp, op = _params(mask, window, doc_ids, visited, mod, alibi_slopes, softcap, boost_radius, boost_factor,
                      rel_bias)
     bms = block_mask.struct() if block_mask is not None else None
@@ -327,18 +386,30 @@ def backward(q, k, v, out, dout, lse, *, scale=None, mask=MASK_NONE, window=0, d
     bias table; its scratch ``rel_bias_ws`` is allocated when not given.  The
     return value is then (dq, dk, dv, rel_bias_grad)."""
     torch = _torch()
-    B, Hq, Sq, D = q.shape
-    Hkv, Skv = k.shape[1], k.shape[2]
-    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    B, Hq, Hkv, Sq, Skv, D = _check_qkv(q, k, v)
+    _check_mod_tensors(q, Hq, Sq, Skv, doc_ids, alibi_slopes, rel_bias)
+    qs, kvs = (B, Hq, Sq, D), (B, Hkv, Skv, D)
+    _dense(out, "out", qs, (q.dtype,), q.device)
+    _dense(dout, "dout", qs, (q.dtype,), q.device)
+    _dense(lse, "lse", (B, Hq, Sq), (torch.float32,), q.device)
+    if grads is None:
+        grads = (torch.empty(qs, dtype=q.dtype, device=q.device), torch.empty(kvs, dtype=q.dtype, device=q.device),
+                 torch.empty(kvs, dtype=q.dtype, device=q.device))
+    dq, dk, dv = grads
+    for t, what, shape in ((dq, "dq", qs), (dk, "dk", kvs), (dv, "dv", kvs)):
+        _dense(t, what, shape, (q.dtype,), q.device)
     ws_bytes = fa_bwd_workspace_bytes(B, Hq, Sq, D)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _dense(workspace, "workspace", None, None, q.device)
     want_bias_grad = rel_bias_grad is not None
     if rel_bias_grad is True:
         rel_bias_grad = torch.empty((Hq, Sq + Skv - 1), dtype=torch.float32, device=q.device)
     if want_bias_grad and rel_bias_ws is None:
         rel_bias_ws = torch.empty(max(fa_bwd_rel_bias_workspace_bytes(B, Hq, Sq, Skv), 16), dtype=torch.uint8,
                                   device=q.device)
+    _dense(rel_bias_grad, "rel_bias_grad", (Hq, Sq + Skv - 1), (torch.float32,), q.device)
+    _dense(rel_bias_ws, "rel_bias_ws", None, None, q.device)
     mp, op = _params(mask, window, doc_ids, None, mod, alibi_slopes, softcap, boost_radius, boost_factor,
                      rel_bias, rel_bias_grad, rel_bias_ws)
     bms = block_mask.struct() if block_mask is not None else None
