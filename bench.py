@@ -12,11 +12,15 @@ stream the library launches on.  The CPU baseline times the fp64 oracle on a
 bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-Prints one JSON line.
+                       [--seq-len S] [--batch B]
+Prints one JSON line.  With --seq-len / --batch the profile-derived fields
+(roofline.traffic, clock) are null: the committed counters are for the
+workload's own shape.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -143,6 +147,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="causal_fwd_bwd")
+    ap.add_argument("--seq-len", type=int, default=0, help="run the workload at this sequence length instead")
+    ap.add_argument("--batch", type=int, default=0, help="run the workload at this batch size instead")
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads of the oracle CPU baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -173,6 +179,9 @@ def main():
     if args.workload not in synth.WORKLOADS:
         sys.exit(f"unknown workload {args.workload}; choose from {sorted(synth.WORKLOADS)}")
     w = synth.WORKLOADS[args.workload]
+    reshaped = bool(args.seq_len or args.batch)
+    if reshaped:
+        w = dataclasses.replace(w, S=args.seq_len or w.S, B=args.batch or w.B)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     q, k, v, extras = synth.workload_inputs(w)
@@ -283,11 +292,11 @@ def main():
         "wall_s": round(wall, 3),
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(w.name, dominant)},
+                     "traffic": None if reshaped else measured_traffic(w.name, dominant)},
     }
     # The peak scaled to the shader clock the profiler saw under this kernel
     # (busy cycles over duration); the nominal peak assumes 2.4 GHz.
-    ghz = measured_profile(w.name, dominant).get("clock_ghz")
+    ghz = None if reshaped else measured_profile(w.name, dominant).get("clock_ghz")
     rec["clock"] = None if ghz is None else {
         "kernel": dominant, "ghz": round(ghz, 3), "peak_at_clock": round(peak * ghz / 2.4, 1),
         "frac_at_clock": round(achieved / (peak * ghz / 2.4), 4)}

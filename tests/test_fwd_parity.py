@@ -66,7 +66,20 @@ def test_variants(name, D, dtype):
     check_lse(lse, l_ref)
 
 
-@pytest.mark.parametrize("S", [1, 2, 63, 64, 127, 128, 129, 200, 257, 511])
+# Above 1024 keys the unmasked, causal and long-window forwards take the
+# 8-wave ping-pong kernel (256-row tiles); every modifier at a size past that.
+PP_VARIANTS = ["none", "causal", "causal_alibi", "softcap", "causal_softcap_small", "boost", "none_alibi"]
+
+
+@pytest.mark.parametrize("name", PP_VARIANTS)
+@pytest.mark.parametrize("D", [64, 128])
+def test_variants_ping_pong_sizes(name, D):
+    (o, lse), o_ref, l_ref = run_case(1, 4, 2, 1300, 1300, D, "bf16", VARIANTS[name], seed=13)
+    check_out(o, o_ref, "bf16")
+    check_lse(lse, l_ref)
+
+
+@pytest.mark.parametrize("S", [1, 2, 63, 64, 127, 128, 129, 200, 257, 511, 1025, 1100, 1537])
 def test_lengths_causal(S):
     (o, lse), o_ref, l_ref = run_case(1, 2, 2, S, S, 128, "bf16", dict(mask=1), seed=S)
     check_out(o, o_ref, "bf16")

@@ -94,6 +94,17 @@ def test_forward(name, D, dtype):
     check_lse(lse, l_ref)
 
 
+@pytest.mark.parametrize("mask", [0, 1])
+@pytest.mark.parametrize("D", [64, 128])
+def test_forward_ping_pong_sizes(mask, D):
+    """Past 1024 keys the unmasked and causal forwards take the ping-pong
+    kernel, whose bias slices are loaded by the group that issues no tiles."""
+    (q, k, v, table, doc, _, scale), (o, lse) = run(1, 4, 2, 1300, 1300, D, dict(mask=mask), 63)
+    o_ref, l_ref = oracle.forward(q, k, v, scale, _variant(dict(mask=mask), doc, table, 1300))
+    check_out(o, o_ref, "bf16")
+    check_lse(lse, l_ref)
+
+
 @pytest.mark.parametrize("Sq,Skv", [(100, 300), (300, 100), (1, 257), (257, 1)])
 @pytest.mark.parametrize("mask", [0, 1])
 def test_forward_sq_ne_skv(Sq, Skv, mask):

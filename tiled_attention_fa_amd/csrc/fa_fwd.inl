@@ -816,8 +816,12 @@ static hipError_t launch_bm(const FwdArgs& a, int mod, hipStream_t st) {
   // short windows that union is up to 25% longer than a 128-row tile's
   // range, and the 4-wave kernel is faster (1024-key window: 0.42 vs
   // 0.44 ms at B2 Hq32 S8192).
+  // Up to 1024 keys a query tile has at most 16 key steps, and the 4-wave
+  // kernel, two workgroups per compute unit, hides each one's prologue and
+  // epilogue behind the other's steps: causal B16 H16 S1024 0.123 against
+  // 0.134 ms (equal at S = 2048, the ping-pong kernel 3-5 % ahead from 4096).
   if constexpr (!F32 && MASK != MASK_DOCUMENT) {
-    if (MASK != MASK_WINDOW || a.mask.window > 2048) return launch_pp<D, MASK>(a, mod, st);
+    if (a.Skv > 1024 && (MASK != MASK_WINDOW || a.mask.window > 2048)) return launch_pp<D, MASK>(a, mod, st);
   }
   return launch_mod<D, F32, MASK, false>(a, mod, st);
 }
