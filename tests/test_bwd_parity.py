@@ -145,3 +145,28 @@ def test_block_mask_unequal_lengths(Sq, Skv, name, D):
     check_out(o, o_ref, "bf16", "O")
     for g, r, what in zip((dq, dk, dv), (rq, rk, rv), ("dQ", "dK", "dV")):
         check_out(g, r, "bf16", what)
+
+
+def test_phases_on_two_streams():
+    """DELTA, then DK/DV and DQ on two streams (each waiting for DELTA by an
+    event), gives the same bits as the single fa_bwd call."""
+    B, Hq, Hkv, S, D = 1, 4, 2, 700, 128
+    q, k, v = (dev(t) for t in synth.qkv(B, Hq, Hkv, S, S, D, 70))
+    do = dev(synth.randn((B, Hq, S, D), 71))
+    spec = dict(mask=fa.MASK_CAUSAL, mod=fa.MOD_ALIBI)
+    o, lse = fa.forward(q, k, v, return_lse=True, **spec)
+    ref = fa.backward(q, k, v, o, do, lse, **spec)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(B, Hq, S, D), dtype=torch.uint8, device="cuda")
+    grads = (torch.full_like(q, float("nan")), torch.full_like(k, float("nan")), torch.full_like(v, float("nan")))
+    main = torch.cuda.current_stream()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    fa.backward(q, k, v, o, do, lse, workspace=ws, grads=grads, phases=fa.FA_BWD_DELTA, stream=main, **spec)
+    s1.wait_stream(main)
+    s2.wait_stream(main)
+    fa.backward(q, k, v, o, do, lse, workspace=ws, grads=grads, phases=fa.FA_BWD_DKDV, stream=s1, **spec)
+    fa.backward(q, k, v, o, do, lse, workspace=ws, grads=grads, phases=fa.FA_BWD_DQ, stream=s2, **spec)
+    main.wait_stream(s1)
+    main.wait_stream(s2)
+    torch.cuda.synchronize()
+    for got, want, what in zip(grads, ref, ("dQ", "dK", "dV")):
+        assert torch.equal(got, want), what
