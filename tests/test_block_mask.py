@@ -151,3 +151,18 @@ def test_orders_change_nothing_but_schedule(mask):
     torch.cuda.synchronize()
     for x, y in zip(*res):
         assert torch.equal(x, y)
+
+
+def test_rebuild_into_overwrites_everything():
+    """Rebuilding into an existing mask (no allocation) for other document ids
+    leaves exactly what a fresh build writes: every array, including the
+    unused list tails, is rewritten."""
+    B, S = 2, 1500
+    first = _docs(B, S, 90, lo=1, hi=60)      # many short documents: long lists
+    second = _docs(B, S, 91, lo=400, hi=900)  # few long ones
+    bm = fa.build_block_mask(3, B, S, S, doc_ids=dev(first))
+    fa.build_block_mask(3, B, S, S, doc_ids=dev(second), into=bm)
+    fresh = fa.build_block_mask(3, B, S, S, doc_ids=dev(second))
+    torch.cuda.synchronize()
+    for name in ("tile_state", "kv_count", "kv_index", "q_count", "q_index", "q_order", "kv_order"):
+        assert torch.equal(getattr(bm, name), getattr(fresh, name)), name
