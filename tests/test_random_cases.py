@@ -27,7 +27,7 @@ def draw(seed):
     spec = dict(mask=mask)
     if mask == 2:
         spec["window"] = int(r.integers(1, 1500))
-    mod = int(r.integers(0, 4))
+    mod = int(r.integers(0, 5))
     if mod:
         spec["mod"] = mod
     if mod == 2:
@@ -38,7 +38,7 @@ def draw(seed):
                 block_mask=bool(r.random() < 0.3))
 
 
-@pytest.mark.parametrize("seed", range(500, 524))
+@pytest.mark.parametrize("seed", range(500, 540))
 def test_random_case(seed):
     c = draw(seed)
     B, Hq, Hkv, Sq, Skv, D, spec = c["B"], c["Hq"], c["Hkv"], c["Sq"], c["Skv"], c["D"], c["spec"]
@@ -49,7 +49,10 @@ def test_random_case(seed):
     bm = None
     if c["block_mask"]:
         bm = fa.build_block_mask(spec["mask"], B, Sq, Skv, window=spec.get("window", 0), doc_ids=dev(doc))
-    var = oracle.Variant(doc_ids=None if doc is None else doc.numpy(), **spec)
+    table = synth.rel_bias_table(Hq, Sq, Skv, seed + 3) if spec.get("mod") == fa.MOD_REL_BIAS else None
+    var = oracle.Variant(doc_ids=None if doc is None else doc.numpy(), **spec,
+                         rel_bias=None if table is None else table.numpy(), rel_origin=Skv - 1)
+    spec = dict(spec, rel_bias=dev(table))
     qd, kd, vd = dev(q), dev(k), dev(v)
     o, lse = fa.forward(qd, kd, vd, scale=scale, doc_ids=dev(doc), block_mask=bm, return_lse=True, **spec)
     torch.cuda.synchronize()
