@@ -165,3 +165,34 @@ def test_incoherent_processing_lowers_error_end_to_end():
         torch.cuda.synchronize()
         rmse[name] = math.sqrt(np.mean((_f64(o) - ref) ** 2))
     assert rmse["plain"] / rmse["incoherent"] >= 1.3, rmse
+
+
+@pytest.mark.parametrize("seed", range(700, 712))
+def test_fp8_random_case(seed):
+    """Seeded random shape, grouping, mask and head dimension, with and
+    without incoherent processing."""
+    r = np.random.default_rng(seed)
+    Hkv = int(r.choice([1, 2, 4]))
+    Hq = Hkv * int(r.choice([1, 2, 4]))
+    B, D = int(r.integers(1, 3)), int(r.choice([64, 128]))
+    Sq, Skv = int(r.integers(1, 1200)), int(r.integers(1, 1200))
+    mask = int(r.integers(0, 3))
+    window = int(r.integers(1, 1300)) if mask == 2 else 0
+    s = synth.signs(D, seed).numpy() if r.random() < 0.5 else None
+    q, _, _ = synth.qkv(B, Hq, Hkv, Sq, Sq, D, seed)
+    _, k, v = synth.qkv(B, Hq, Hkv, Skv, Skv, D, seed + 1)
+    q8, qs = ofp8.block_quantize(_f64(q).reshape(B * Hq, Sq, D), s)
+    k8, ks = ofp8.block_quantize(_f64(k).reshape(B * Hkv, Skv, D), s)
+    v8, vs = ofp8.block_quantize(_f64(v).reshape(B * Hkv, Skv, D))
+
+    def gpu(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    o, lse = fa.forward_fp8(gpu(q8).view(B, Hq, Sq, D), gpu(k8).view(B, Hkv, Skv, D), gpu(v8).view(B, Hkv, Skv, D),
+                            gpu(qs), gpu(ks), gpu(vs), scale=f32_scale(D), mask=mask, window=window,
+                            return_lse=True)
+    torch.cuda.synchronize()
+    O, L = ofp8.fp8_forward(q8, k8, v8, qs, ks, vs, f32_scale(D), oracle.Variant(mask=mask, window=window),
+                            Hq=Hq, Hkv=Hkv)
+    _check_fp8_out(o.cpu().view(B * Hq, Sq, D), O, np.abs(ofp8.dequantize(v8, vs)).max())
+    check_lse(lse.cpu().view(B * Hq, Sq), L)
