@@ -11,6 +11,7 @@ import tiled_attention_fa_amd as fa
 from tests.floors import backward_floors
 from tests.gpu_util import check_lse, check_out, dev, f32_scale
 from tests.test_fwd_parity import doc_ids_for
+from tests.test_rel_bias_parity import _error_scales, check_grad
 
 pytestmark = pytest.mark.gpu
 
@@ -62,8 +63,14 @@ def test_random_case(seed):
     if c["dtype"] != "bf16":
         return
     do = synth.randn((B, Hq, Sq, D), seed + 2)
-    dq, dk, dv = fa.backward(qd, kd, vd, o, dev(do), lse, scale=scale, doc_ids=dev(doc), block_mask=bm, **spec)
+    rel = table is not None
+    res = fa.backward(qd, kd, vd, o, dev(do), lse, scale=scale, doc_ids=dev(doc), block_mask=bm,
+                      rel_bias_grad=True if rel else None, **spec)
     torch.cuda.synchronize()
+    dq, dk, dv = res[:3]
+    if rel:
+        check_grad(res[3], oracle.rel_bias_grad(q, k, v, do, scale, var), _error_scales(q, k, v, do, scale, var),
+                   f"rel_bias_grad {c}")
     rq, rk, rv = oracle.backward(q, k, v, do, scale, var)
     # Where many rows weigh the same keys (|dK|, |dV| of 10-40) the bf16
     # roundings of the data path alone exceed 2e-2; the bar is then 1.5x
