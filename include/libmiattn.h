@@ -96,7 +96,8 @@ typedef struct {
 typedef struct {
   const float* alibi_slopes; /* device float [Hq]; NULL: 2^(-8(h+1)/Hq) */
   float softcap;             /* FA_MOD_SOFTCAP: > 0 */
-  int32_t boost_radius;      /* FA_MOD_LOCAL_BOOST: >= 0 */
+  int32_t boost_radius;      /* FA_MOD_LOCAL_BOOST: >= 0; 0 boosts no pair, and
+                                any value >= max(Sq, Skv) boosts every pair */
   float boost_factor;        /* FA_MOD_LOCAL_BOOST: finite */
   const float* rel_bias;     /* FA_MOD_REL_BIAS: device float [Hq][Sq + Skv - 1],
                                 entry i - j + Skv - 1 is added to the scaled

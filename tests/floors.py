@@ -48,3 +48,10 @@ def backward_floors(q, k, v, do, scale, var):
             dv_e[b, hk] += P.T @ dO
             dv_r[b, hk] += _bf16(P).T @ dO
     return _beyond(dq_r, dq_e), _beyond(dk_r, dk_e), _beyond(dv_r, dv_e)
+
+
+def rounding_mean(exact):
+    """Mean |bf16(x) - x| over an exact output: what rounding the result to
+    bf16 alone adds to the mean error, before any arithmetic error."""
+    x = np.asarray(exact, dtype=np.float64)
+    return float(np.mean(np.abs(_bf16(x) - x))) if x.size else 0.0

@@ -6,6 +6,7 @@ import torch
 import oracle
 import synth
 import tiled_attention_fa_amd as fa
+from tests.floors import backward_floors, rounding_mean
 from tests.gpu_util import check_out, dev, f32_scale
 from tests.test_fwd_parity import VARIANTS, doc_ids_for
 
@@ -52,6 +53,25 @@ def test_variants(name, D):
     got, ref = run_bwd(1, 4, 2, 333, D, VARIANTS[name], seed=21)
     for g, r, what in zip(got, ref, ("dQ", "dK", "dV")):
         check_out(g, r, "bf16", what, max_excess=MAX_EXCESS.get(name))
+
+
+@pytest.mark.parametrize("radius", [0, 1, 333, 2**31 - 1])
+@pytest.mark.parametrize("mask", [0, 1])
+def test_boost_radius_edges(radius, mask):
+    """Local boost with radius 0 (no pair boosted), 1 (the diagonal only) and
+    radii covering every pair, the last past int arithmetic on the radius."""
+    spec = dict(mask=mask, mod=3, boost_radius=radius, boost_factor=2.0)
+    seed = radius % 1000 + 5
+    got, ref = run_bwd(1, 2, 1, 333, 128, spec, seed=seed)
+    # A factor of 2 on every pair doubles the effective scale, and the bf16
+    # operands alone then leave up to ~3e-2 on dQ / dK (causal): such cases
+    # are held to 1.5x their floor, as the seeded random cases are.
+    q, k, v = synth.qkv(1, 2, 1, 333, 333, 128, seed)
+    floors = backward_floors(q, k, v, synth.randn((1, 2, 333, 128), seed + 100), f32_scale(128),
+                             oracle.Variant(**spec))
+    for g, r, what, fl in zip(got, ref, ("dQ", "dK", "dV"), floors):
+        check_out(g, r, "bf16", f"{what} floor {fl:.2e}", max_excess=max(2e-2, 1.5 * fl),
+                  rounding_mean=rounding_mean(r) > 1e-3)
 
 
 @pytest.mark.parametrize("S", [1, 64, 127, 129, 260])

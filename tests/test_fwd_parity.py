@@ -106,6 +106,25 @@ def test_sq_ne_skv_modifiers(Sq, Skv, name, D, dtype):
     check_lse(lse, l_ref)
 
 
+# Local boost at the edges of its radius: 0 (no pair boosted, the unmodified
+# scores), 1 (the diagonal only), and radii at and far past every |i - j|
+# (all pairs boosted; 2^31 - 1 would overflow radius arithmetic done in int).
+BOOST_EDGES = [0, 1, 699, 700 + 333, 2**31 - 1]
+
+
+@pytest.mark.parametrize("radius", BOOST_EDGES)
+@pytest.mark.parametrize("mask", [0, 1])
+@pytest.mark.parametrize("Sq,D,dtype", [(333, 128, "bf16"), (700, 64, "f32"), (1300, 128, "bf16")])
+def test_boost_radius_edges(radius, mask, Sq, D, dtype):
+    """Sq = 1300 takes the ping-pong kernel, the others the 4-wave kernel;
+    keys 333 long except at Sq = 1300 (Skv = Sq)."""
+    Skv = Sq if Sq == 1300 else 333
+    spec = dict(mask=mask, mod=3, boost_radius=radius, boost_factor=2.0)
+    (o, lse), o_ref, l_ref = run_case(1, 2, 1, Sq, Skv, D, dtype, spec, seed=radius % 1000 + Sq)
+    check_out(o, o_ref, dtype)
+    check_lse(lse, l_ref)
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 4), (8, 2), (8, 1)])
 @pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "f32")])
 def test_gqa_ratios(Hq, Hkv, D, dtype):

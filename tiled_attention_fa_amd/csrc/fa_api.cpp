@@ -2,6 +2,7 @@
 // dispatch to the template instantiations.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -82,7 +83,10 @@ int check_variant(int B, int Hq, int Sq, int Skv, float scale, int mask_kind, co
     case FA_MOD_LOCAL_BOOST:
       if (!op) return FA_ERR_NULL;
       if (op->boost_radius < 0 || !std::isfinite(op->boost_factor)) return FA_ERR_PARAM;
-      mod.boost_radius = op->boost_radius;
+      // Every pair has |i - j| < max(Sq, Skv), so a larger radius selects the
+      // same pairs; the clamp keeps the kernels' band arithmetic (2 R and
+      // first-row + R) far from int overflow.  R = 0 selects no pair.
+      mod.boost_radius = (int)std::min<long long>(op->boost_radius, std::max<long long>(std::max(Sq, Skv), 1));
       mod.boost_factor = op->boost_factor;
       break;
     case FA_MOD_REL_BIAS:
@@ -95,6 +99,12 @@ int check_variant(int B, int Hq, int Sq, int Skv, float scale, int mask_kind, co
   (void)B;
   (void)Hq;
   return FA_OK;
+}
+
+// The modifier the kernels run: a local boost of radius 0 boosts no pair,
+// which is the unmodified score (and gradient), so it takes that path.
+int kernel_mod(int mod_kind, const ModArgs& mod) {
+  return (mod_kind == FA_MOD_LOCAL_BOOST && mod.boost_radius == 0) ? FA_MOD_NONE : mod_kind;
 }
 
 int check_block_mask(const fa_block_mask* bm, int mask_kind, int B, int Sq, int Skv, bool need_q_lists,
@@ -183,13 +193,12 @@ int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, i
   a.scale = scale;
   a.scale_log2 = log2_multiplier(scale);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int mod = kernel_mod(score_mod_kind, a.mod);
   hipError_t e;
   if (dtype == FA_BF16)
-    e = D == 128 ? launch_fwd_dt<128, false>(a, mask_kind, score_mod_kind, st)
-                 : launch_fwd_dt<64, false>(a, mask_kind, score_mod_kind, st);
+    e = D == 128 ? launch_fwd_dt<128, false>(a, mask_kind, mod, st) : launch_fwd_dt<64, false>(a, mask_kind, mod, st);
   else
-    e = D == 128 ? launch_fwd_dt<128, true>(a, mask_kind, score_mod_kind, st)
-                 : launch_fwd_dt<64, true>(a, mask_kind, score_mod_kind, st);
+    e = D == 128 ? launch_fwd_dt<128, true>(a, mask_kind, mod, st) : launch_fwd_dt<64, true>(a, mask_kind, mod, st);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -328,8 +337,9 @@ int fa_bwd_phase(int phase, const void* q, const void* k, const void* v, const v
   a.scale = scale;
   a.scale_log2 = log2_multiplier(scale);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const hipError_t e = D == 128 ? launch_bwd_d<128>(a, mask_kind, score_mod_kind, phase, st)
-                                : launch_bwd_d<64>(a, mask_kind, score_mod_kind, phase, st);
+  const int mod = kernel_mod(score_mod_kind, a.mod);
+  const hipError_t e = D == 128 ? launch_bwd_d<128>(a, mask_kind, mod, phase, st)
+                                : launch_bwd_d<64>(a, mask_kind, mod, phase, st);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

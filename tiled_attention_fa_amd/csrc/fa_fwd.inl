@@ -57,8 +57,9 @@ __device__ __forceinline__ float transform_scores(f32x16 (&st)[NT], int partial,
   float mb = kNegInf;
   bool plain = MOD == MOD_NONE;
   if constexpr (MOD == MOD_BOOST) {
+    // Steps with no pair in the band |i - j| < R (none at all when R = 0).
     const int R = a.mod.boost_radius;
-    plain = !(k0 + 32 * NT - 1 > qw0 - R && k0 < qw0 + 31 + R);
+    plain = R <= 0 || !(k0 + 32 * NT - 1 > qw0 - R && k0 < qw0 + 31 + R);
   }
   // Elementwise mask, one branch per mode for the whole step.
   auto mask_all = [&](float masked) __attribute__((always_inline)) {
@@ -123,6 +124,9 @@ __device__ __forceinline__ float transform_scores(f32x16 (&st)[NT], int partial,
           if constexpr (MOD == MOD_ALIBI) {
             x = __builtin_fmaf(st[t][r], c1, e ? bq + s2e[e] : bq);
           } else if constexpr (MOD == MOD_BOOST) {
+            // |d| < R as one unsigned compare: d + R - 1 in [0, 2R - 2].
+            // Valid for R >= 1 (R = 0 took the plain form above); the host
+            // clamps R to max(Sq, Skv), so 2R - 1 cannot overflow.
             const int d = d0 + c;  // j - i
             x = st[t][r] * ((unsigned)(d + R - 1) < (unsigned)(2 * R - 1) ? cf : c1);
           } else {
