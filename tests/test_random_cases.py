@@ -8,7 +8,7 @@ import torch
 import oracle
 import synth
 import tiled_attention_fa_amd as fa
-from tests.floors import backward_floors
+from tests.floors import backward_floors, rounding_mean
 from tests.gpu_util import check_lse, check_out, dev, f32_scale
 from tests.test_fwd_parity import doc_ids_for
 from tests.test_rel_bias_parity import _error_scales, check_grad
@@ -74,7 +74,12 @@ def test_random_case(seed):
     rq, rk, rv = oracle.backward(q, k, v, do, scale, var)
     # Where many rows weigh the same keys (|dK|, |dV| of 10-40) the bf16
     # roundings of the data path alone exceed 2e-2; the bar is then 1.5x
-    # that floor (tests/floors.py).
+    # that floor (tests/floors.py).  The mean is taken beyond the output's
+    # own rounding only where that rounding alone takes more than half of the
+    # 2e-3 mean bar (outputs of magnitude ~2 and up); elsewhere it is the
+    # plain mean.
     floors = backward_floors(q, k, v, do, scale, var)
     for g, r, what, fl in zip((dq, dk, dv), (rq, rk, rv), ("dQ", "dK", "dV"), floors):
-        check_out(g, r, "bf16", f"{what} {c} floor {fl:.2e}", max_excess=max(2e-2, 1.5 * fl), rounding_mean=True)
+        rm = rounding_mean(r)
+        check_out(g, r, "bf16", f"{what} {c} floor {fl:.2e} rounding mean {rm:.2e}", max_excess=max(2e-2, 1.5 * fl),
+                  rounding_mean=rm > 1e-3)
