@@ -20,7 +20,16 @@ def built():
     if not os.path.exists(binding.LIB_PATH):
         from tiled_attention_fa_amd import build
         build.build()
-    return fa.lib()
+    alt = os.environ.get("MIATTN_ABI_TEST_LIB")
+    if alt:
+        # The validation layer built on its own with the host sanitizers and
+        # launchers that only report failure (tests/test_abi_sanitized.py):
+        # the calls below exercise it instead of the GPU library's copy.
+        binding._LIB = binding.declare_prototypes(ctypes.CDLL(alt))
+        yield binding._LIB
+        binding._LIB = None
+        return
+    yield fa.lib()
 
 
 def declared():

@@ -69,42 +69,47 @@ def lib() -> ctypes.CDLL:
     if _LIB is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m tiled_attention_fa_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        L.fa_fwd.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
-                             _I, ctypes.POINTER(FaMaskParams), _I, ctypes.POINTER(FaModParams),
-                             ctypes.POINTER(FaBlockMask), _P]
-        L.fa_fwd.restype = _I
-        L.fa_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
-                             _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
-                             _I, ctypes.POINTER(FaMaskParams), _I, ctypes.POINTER(FaModParams),
-                             ctypes.POINTER(FaBlockMask), _P]
-        L.fa_bwd.restype = _I
-        L.fa_bwd_phase.argtypes = [_I] + L.fa_bwd.argtypes
-        L.fa_bwd_phase.restype = _I
-        L.fa_bwd_workspace_bytes.argtypes = [_I, _I, _I, _I]
-        L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
-        L.fa_bwd_rel_bias_workspace_bytes.argtypes = [_I, _I, _I, _I]
-        L.fa_bwd_rel_bias_workspace_bytes.restype = ctypes.c_size_t
-        L.fa_block_mask_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
-        L.fa_block_mask_bytes.restype = ctypes.c_size_t
-        L.fa_block_mask_layout.argtypes = [_P, _I, _I, _I, _I, _I, _I, ctypes.POINTER(FaBlockMask)]
-        L.fa_block_mask_layout.restype = _I
-        L.fa_block_mask_build.argtypes = [_I, ctypes.POINTER(FaMaskParams), _I, _I, _I,
-                                          ctypes.POINTER(FaBlockMask), _P]
-        L.fa_block_mask_build.restype = _I
-        L.fa_status_str.argtypes = [_I]
-        L.fa_status_str.restype = ctypes.c_char_p
-        L.fa_fwd_kv_step.argtypes = [_I, _I]
-        L.fa_fwd_kv_step.restype = _I
-        L.fa_version.argtypes = []
-        L.fa_version.restype = _I
-        L.fa_fp8_quantize.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P]
-        L.fa_fp8_quantize.restype = _I
-        L.fa_fwd_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float,
-                                 _I, ctypes.POINTER(FaMaskParams), _P]
-        L.fa_fwd_fp8.restype = _I
-        _LIB = L
+        _LIB = declare_prototypes(ctypes.CDLL(LIB_PATH))
     return _LIB
+
+
+def declare_prototypes(L: ctypes.CDLL) -> ctypes.CDLL:
+    """Set the argument and result types of every entry point on a loaded
+    copy of the library; returns it."""
+    L.fa_fwd.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
+                         _I, ctypes.POINTER(FaMaskParams), _I, ctypes.POINTER(FaModParams),
+                         ctypes.POINTER(FaBlockMask), _P]
+    L.fa_fwd.restype = _I
+    L.fa_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                         _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
+                         _I, ctypes.POINTER(FaMaskParams), _I, ctypes.POINTER(FaModParams),
+                         ctypes.POINTER(FaBlockMask), _P]
+    L.fa_bwd.restype = _I
+    L.fa_bwd_phase.argtypes = [_I] + L.fa_bwd.argtypes
+    L.fa_bwd_phase.restype = _I
+    L.fa_bwd_workspace_bytes.argtypes = [_I, _I, _I, _I]
+    L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.fa_bwd_rel_bias_workspace_bytes.argtypes = [_I, _I, _I, _I]
+    L.fa_bwd_rel_bias_workspace_bytes.restype = ctypes.c_size_t
+    L.fa_block_mask_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
+    L.fa_block_mask_bytes.restype = ctypes.c_size_t
+    L.fa_block_mask_layout.argtypes = [_P, _I, _I, _I, _I, _I, _I, ctypes.POINTER(FaBlockMask)]
+    L.fa_block_mask_layout.restype = _I
+    L.fa_block_mask_build.argtypes = [_I, ctypes.POINTER(FaMaskParams), _I, _I, _I,
+                                      ctypes.POINTER(FaBlockMask), _P]
+    L.fa_block_mask_build.restype = _I
+    L.fa_status_str.argtypes = [_I]
+    L.fa_status_str.restype = ctypes.c_char_p
+    L.fa_fwd_kv_step.argtypes = [_I, _I]
+    L.fa_fwd_kv_step.restype = _I
+    L.fa_version.argtypes = []
+    L.fa_version.restype = _I
+    L.fa_fp8_quantize.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P]
+    L.fa_fp8_quantize.restype = _I
+    L.fa_fwd_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float,
+                             _I, ctypes.POINTER(FaMaskParams), _P]
+    L.fa_fwd_fp8.restype = _I
+    return L
 
 
 # ---------------------------------------------------------------- raw C calls
