@@ -12,7 +12,7 @@ stream the library launches on.  The CPU baseline times the fp64 oracle on a
 bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--seq-len S] [--batch B]
+                       [--seq-len S] [--batch B] [--oracle full]
 Prints one JSON line.  With --seq-len / --batch the profile-derived fields
 (roofline.traffic, clock) are null: the committed counters are for the
 workload's own shape.
@@ -68,46 +68,137 @@ def measured_traffic(workload: str, kernel: str):
     return measured_profile(workload, kernel).get("bytes_per_launch")
 
 
-def cpu_baseline(w, heads: int):
-    """The oracle (numpy fp64, as committed) on `heads` whole (batch, head)
-    pairs of the workload; returns the dict for the JSON line."""
-    import numpy as np
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
-    import oracle
-    import synth
-    from tiled_attention_fa_amd import flops
 
+def affinity_cores() -> int:
+    """Host cores this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover - non-Linux
+        return os.cpu_count() or 1
+
+
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover - threadpoolctl is optional
-        threads = os.cpu_count() or 1
-    q, k, v, extras = synth.workload_inputs(w)
-    doc = extras.get("doc_ids")
-    var = oracle.Variant(mask=w.mask, window=w.window, mod=w.mod, softcap=w.softcap,
-                         boost_radius=w.boost_radius, boost_factor=w.boost_factor,
-                         doc_ids=None if doc is None else doc.numpy())
-    from tiled_attention_fa_amd.binding import default_scale
-    scale = default_scale(w.D)
-    G = w.Hq // w.Hkv
+        return os.cpu_count() or 1
+
+
+class _OracleJob:
+    """The oracle's work for whole (batch, head) pairs of one workload: the
+    inputs are generated once per process from the workload's seeds."""
+
+    def __init__(self, w):
+        import oracle
+        import synth
+        from tiled_attention_fa_amd.binding import default_scale
+
+        self.w = w
+        self.q, self.k, self.v, self.extras = synth.workload_inputs(w)
+        doc = self.extras.get("doc_ids")
+        self.var = oracle.Variant(mask=w.mask, window=w.window, mod=w.mod, softcap=w.softcap,
+                                  boost_radius=w.boost_radius, boost_factor=w.boost_factor,
+                                  doc_ids=None if doc is None else doc.numpy())
+        self.scale = default_scale(w.D)
+
+    def head_flops(self) -> float:
+        """Admissible-pair FLOPs of one (batch, head): 4 D per pair forward, + 10 D backward."""
+        from tiled_attention_fa_amd import flops
+        w = self.w
+        per_head = flops.pairs_per_row_batch(w.mask, w.S, w.S, w.window, self.extras.get("doc_lengths"))
+        return float(per_head * ((4 + 10) * w.D if w.backward else 4 * w.D))
+
+    def run(self, b: int, h: int) -> None:
+        import oracle
+        w, q, k, v = self.w, self.q, self.k, self.v
+        hk = h // (w.Hq // w.Hkv)
+        if w.backward:
+            oracle.backward_head(q[b, h], k[b, hk], v[b, hk], self.extras["do"][b, h], self.scale, self.var,
+                                 b, h, w.Hq)
+        else:
+            oracle.forward(q[b:b + 1, h:h + 1], k[b:b + 1, hk:hk + 1], v[b:b + 1, hk:hk + 1], self.scale, self.var)
+
+
+def cpu_baseline(w, heads: int):
+    """The oracle (numpy fp64, as committed) on `heads` whole (batch, head)
+    pairs of the workload with the BLAS library's threads, plus one head on a
+    single core (pairs per second per core); returns the dict for the JSON line."""
+    from threadpoolctl import threadpool_limits
+
+    job = _OracleJob(w)
+    threads = _blas_threads()
+    info = {"cpu_model": cpu_model(), "affinity_cores": affinity_cores()}
     if w.dtype == "fp8":
-        return _cpu_baseline_fp8(w, q, k, v, var, scale, max(1, heads // 16), threads)  # ~20 s a head
+        return {**_cpu_baseline_fp8(w, job.q, job.k, job.v, job.var, job.scale, max(1, heads // 16), threads),
+                **info}  # ~20 s a head
     todo = [(0, h) for h in range(min(heads, w.Hq))]
     t0 = time.perf_counter()
     for b, h in todo:
-        hk = h // G
-        if w.backward:
-            oracle.backward_head(q[b, h], k[b, hk], v[b, hk], extras["do"][b, h], scale, var, b, h, w.Hq)
-        else:
-            oracle.forward(q[b:b + 1, h:h + 1], k[b:b + 1, hk:hk + 1], v[b:b + 1, hk:hk + 1], scale, var)
+        job.run(b, h)
     dt = time.perf_counter() - t0
-    per_head = flops.pairs_per_row_batch(w.mask, w.S, w.S, w.window, extras.get("doc_lengths"))
-    work = per_head * len(todo) * ((4 + 10) * w.D if w.backward else 4 * w.D)
-    return {"value": work / dt / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
-            "seconds": dt,
+    hf = job.head_flops()
+    pairs_per_head = hf / ((4 + 10) * w.D if w.backward else 4 * w.D)
+    # One more head on one core: the per-core rate, free of BLAS threading.
+    with threadpool_limits(1):
+        t1 = time.perf_counter()
+        job.run(0, min(heads, w.Hq) % w.Hq)
+        dt1 = time.perf_counter() - t1
+    return {"value": hf * len(todo) / dt / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+            "seconds": dt, **info,
+            "per_core": {"pairs_per_s": pairs_per_head / dt1, "tflops": hf / dt1 / 1e12, "seconds": dt1,
+                         "sample": "one more (batch, head) pair, BLAS limited to one thread"},
             "sample": f"{'forward+backward' if w.backward else 'forward'} of {len(todo)} of {w.B * w.Hq} "
                       f"(batch, head) pairs at full S={w.S}, numpy float64 with {threads} BLAS threads; "
                       f"value = admissible-pair FLOPs of that sample / its time"}
+
+
+def _full_worker(args):
+    """One process of the full oracle run: BLAS on one thread, a share of the heads."""
+    name, heads = args
+    import synth
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        job = _OracleJob(synth.WORKLOADS[name])
+        t0 = time.perf_counter()
+        for b, h in heads:
+            job.run(b, h)
+        return time.perf_counter() - t0
+
+
+def oracle_full(name: str, procs: int) -> dict:
+    """Every (batch, head) pair of the workload through the oracle, one
+    single-threaded process per core (no threads inside the oracle)."""
+    import multiprocessing as mp
+
+    import synth
+    w = synth.WORKLOADS[name]
+    if w.dtype == "fp8":
+        raise SystemExit("--oracle full covers the bf16 and fp32 workloads")
+    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    procs = max(1, min(procs, len(heads)))
+    shares = [heads[i::procs] for i in range(procs)]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(procs) as pool:
+        busy = pool.map(_full_worker, [(name, sh) for sh in shares])
+    wall = time.perf_counter() - t0
+    hf = _OracleJob(w).head_flops()
+    return {"workload": name, "kind": "oracle", "mode": "full", "heads": len(heads), "processes": procs,
+            "cpu_model": cpu_model(), "affinity_cores": affinity_cores(), "wall_s": round(wall, 2),
+            "busy_s_per_process": [round(x, 2) for x in busy], "tflops": hf * len(heads) / wall / 1e12,
+            "pairs_per_s_per_core": hf / ((4 + 10) * w.D if w.backward else 4 * w.D) * len(heads) / sum(busy)}
 
 
 def _cpu_baseline_fp8(w, q, k, v, var, scale, heads, threads):
@@ -150,6 +241,10 @@ def main():
     ap.add_argument("--seq-len", type=int, default=0, help="run the workload at this sequence length instead")
     ap.add_argument("--batch", type=int, default=0, help="run the workload at this batch size instead")
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads of the oracle CPU baseline sample")
+    ap.add_argument("--oracle", choices=["sample", "full"], default="sample",
+                    help="full: only run the oracle over every head of the workload, one single-threaded "
+                         "process per host core (up to --oracle-procs), print one JSON line, no GPU work")
+    ap.add_argument("--oracle-procs", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times) and exit: the reference for "
@@ -159,6 +254,11 @@ def main():
     if args.gpus != 1 or world != 1:
         print("bench.py: the library runs on one GPU (no multi-GPU path); use --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.oracle == "full":
+        print(json.dumps({"oracle_full": oracle_full(args.workload, min(args.oracle_procs, affinity_cores()))}),
+              flush=True)
+        return
 
     import torch
 
