@@ -56,7 +56,9 @@ typedef enum {
   FA_ERR_ALIGN = -4,       /* a device pointer is not 16-byte aligned */
   FA_ERR_PARAM = -5,       /* mask or modifier parameter out of range */
   FA_ERR_WORKSPACE = -6,   /* workspace missing or too small */
-  FA_ERR_LAUNCH = -7       /* the kernel launch failed */
+  FA_ERR_LAUNCH = -7,      /* the kernel launch failed */
+  FA_ERR_SCRATCH = -8      /* fa_bwd_noalloc: the problem's workspace exceeds
+                              FA_NOALLOC_SCRATCH_BYTES */
 } fa_status;
 
 typedef enum { FA_BF16 = 0, FA_F32 = 1 } fa_dtype;
@@ -195,6 +197,31 @@ int fa_bwd_phase(int phase, const void* q, const void* k, const void* v, const v
                  const fa_block_mask* block_mask, void* stream);
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq, int D);
+
+/* Size of the fixed device scratch of fa_bwd_noalloc: 16 MiB per GPU, which
+ * holds the backward workspace of up to B * Hq * Sq = 2^21 query rows. */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* fa_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops, harnesses
+ * that forbid allocation).  The workspace fa_bwd takes from the caller
+ * (fa_bwd_workspace_bytes(B, Hq, Sq, D) bytes) lives instead in a device
+ * array of FA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends; its address is looked up on the first
+ * call on each device.  Nothing is allocated by the call (the relative-bias
+ * gradient still takes its scratch from mod_params, as in fa_bwd).  Returns
+ * FA_ERR_SCRATCH, before any HIP call, when the workspace would exceed
+ * FA_NOALLOC_SCRATCH_BYTES; otherwise the same validation, results and
+ * errors as fa_bwd (identical bits: the same kernels).  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (e.g. on
+ * two streams) race and must be serialised by the caller.  The array needs
+ * no clearing: each call overwrites what it reads. */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv,
+                   int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype, float scale,
+                   int mask_kind, const fa_mask_params* mask_params,
+                   int score_mod_kind, const fa_mod_params* mod_params,
+                   const fa_block_mask* block_mask, void* stream);
 
 /* Size of the scratch a relative-bias gradient needs (fa_mod_params
  * rel_bias_ws): one float row of Skv + 128 per (batch, query head, 128-row

@@ -31,5 +31,6 @@ hipError_t launch_fp8_fwd(const Fp8FwdArgs&, int, hipStream_t) { return hipError
 hipError_t launch_fp8_quantize(const void*, void*, uint8_t*, int, int, int, const float*, hipStream_t) {
   return hipErrorLaunchFailure;
 }
+hipError_t scratch_address(void**) { return hipErrorNotSupported; }
 
 }  // namespace miattn

@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmiattn.so")
 
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED = 0, -1, -2, -3
-FA_ERR_ALIGN, FA_ERR_PARAM, FA_ERR_WORKSPACE, FA_ERR_LAUNCH = -4, -5, -6, -7
+FA_ERR_ALIGN, FA_ERR_PARAM, FA_ERR_WORKSPACE, FA_ERR_LAUNCH, FA_ERR_SCRATCH = -4, -5, -6, -7, -8
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20
 FA_BF16, FA_F32 = 0, 1
 MASK_NONE, MASK_CAUSAL, MASK_SLIDING_WINDOW, MASK_DOCUMENT = 0, 1, 2, 3
 MOD_NONE, MOD_ALIBI, MOD_SOFTCAP, MOD_LOCAL_BOOST, MOD_REL_BIAS = 0, 1, 2, 3, 4
@@ -26,7 +27,7 @@ BLOCK = 128
 
 FA_BWD_DELTA, FA_BWD_DKDV, FA_BWD_DQ = 1, 2, 4
 
-EXPORTED = ("fa_fwd", "fa_fwd_kv_step", "fa_bwd", "fa_bwd_phase", "fa_bwd_workspace_bytes",
+EXPORTED = ("fa_fwd", "fa_fwd_kv_step", "fa_bwd", "fa_bwd_phase", "fa_bwd_noalloc", "fa_bwd_workspace_bytes",
             "fa_bwd_rel_bias_workspace_bytes",
             "fa_block_mask_bytes", "fa_block_mask_layout", "fa_block_mask_build", "fa_fp8_quantize", "fa_fwd_fp8",
             "fa_status_str", "fa_version")
@@ -87,6 +88,8 @@ def declare_prototypes(L: ctypes.CDLL) -> ctypes.CDLL:
     L.fa_bwd.restype = _I
     L.fa_bwd_phase.argtypes = [_I] + L.fa_bwd.argtypes
     L.fa_bwd_phase.restype = _I
+    L.fa_bwd_noalloc.argtypes = L.fa_bwd.argtypes[:9] + L.fa_bwd.argtypes[11:]
+    L.fa_bwd_noalloc.restype = _I
     L.fa_bwd_workspace_bytes.argtypes = [_I, _I, _I, _I]
     L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.fa_bwd_rel_bias_workspace_bytes.argtypes = [_I, _I, _I, _I]
@@ -120,6 +123,10 @@ def fa_fwd(*args) -> int:
 
 def fa_bwd(*args) -> int:
     return lib().fa_bwd(*args)
+
+
+def fa_bwd_noalloc(*args) -> int:
+    return lib().fa_bwd_noalloc(*args)
 
 
 def fa_bwd_phase(*args) -> int:
@@ -382,11 +389,13 @@ def backward(q, k, v, out, dout, lse, *, scale=None, mask=MASK_NONE, window=0, d
              mod=MOD_NONE, alibi_slopes=None, softcap=0.0, boost_radius=0, boost_factor=1.0,
              rel_bias=None, rel_bias_grad=None, rel_bias_ws=None,
              block_mask=None, workspace=None, grads=None, stream=None,
-             phases=FA_BWD_DELTA | FA_BWD_DKDV | FA_BWD_DQ):
+             phases=FA_BWD_DELTA | FA_BWD_DKDV | FA_BWD_DQ, noalloc=False):
     """(dq, dk, dv) of sum(O * dout), recomputing P from ``lse``.
 
     ``phases`` selects which of the three backward launches run (all by
-    default, which is fa_bwd).  With MOD_REL_BIAS, ``rel_bias_grad`` (float32
+    default, which is fa_bwd).  ``noalloc``: call fa_bwd_noalloc, whose
+    workspace is the library's fixed device scratch (all phases; with
+    ``grads`` given and no relative-bias gradient nothing is allocated).  With MOD_REL_BIAS, ``rel_bias_grad`` (float32
     [Hq, Sq + Skv - 1], or True to allocate it) receives the gradient of the
     bias table; its scratch ``rel_bias_ws`` is allocated when not given.  The
     return value is then (dq, dk, dv, rel_bias_grad)."""
@@ -403,10 +412,14 @@ def backward(q, k, v, out, dout, lse, *, scale=None, mask=MASK_NONE, window=0, d
     dq, dk, dv = grads
     for t, what, shape in ((dq, "dq", qs), (dk, "dk", kvs), (dv, "dv", kvs)):
         _dense(t, what, shape, (q.dtype,), q.device)
-    ws_bytes = fa_bwd_workspace_bytes(B, Hq, Sq, D)
-    if workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    _dense(workspace, "workspace", None, None, q.device)
+    if noalloc:
+        if workspace is not None or phases != FA_BWD_DELTA | FA_BWD_DKDV | FA_BWD_DQ:
+            raise ValueError("noalloc: the workspace is the library's own, and every phase runs")
+    else:
+        ws_bytes = fa_bwd_workspace_bytes(B, Hq, Sq, D)
+        if workspace is None:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        _dense(workspace, "workspace", None, None, q.device)
     want_bias_grad = rel_bias_grad is not None
     if rel_bias_grad is True:
         rel_bias_grad = torch.empty((Hq, Sq + Skv - 1), dtype=torch.float32, device=q.device)
@@ -418,13 +431,18 @@ def backward(q, k, v, out, dout, lse, *, scale=None, mask=MASK_NONE, window=0, d
     mp, op = _params(mask, window, doc_ids, None, mod, alibi_slopes, softcap, boost_radius, boost_factor,
                      rel_bias, rel_bias_grad, rel_bias_ws)
     bms = block_mask.struct() if block_mask is not None else None
-    rc = fa_bwd_phase(int(phases), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                _ptr(workspace), workspace.numel() * workspace.element_size(),
-                B, Hq, Hkv, Sq, Skv, D, _dtype_code(q), float(default_scale(D) if scale is None else scale),
-                int(mask), ctypes.byref(mp), int(mod), ctypes.byref(op),
-                ctypes.byref(bms) if bms is not None else None, _stream(stream))
-    if rc != FA_OK:
-        raise FaError(rc, "fa_bwd_phase")
+    tail = (B, Hq, Hkv, Sq, Skv, D, _dtype_code(q), float(default_scale(D) if scale is None else scale),
+            int(mask), ctypes.byref(mp), int(mod), ctypes.byref(op),
+            ctypes.byref(bms) if bms is not None else None, _stream(stream))
+    tensors = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv))
+    if noalloc:
+        rc = fa_bwd_noalloc(*tensors, *tail)
+        if rc != FA_OK:
+            raise FaError(rc, "fa_bwd_noalloc")
+    else:
+        rc = fa_bwd_phase(int(phases), *tensors, _ptr(workspace), workspace.numel() * workspace.element_size(), *tail)
+        if rc != FA_OK:
+            raise FaError(rc, "fa_bwd_phase")
     if want_bias_grad:
         return dq, dk, dv, rel_bias_grad
     return dq, dk, dv

@@ -148,6 +148,7 @@ const char* fa_status_str(int s) {
     case FA_ERR_PARAM: return "a mask or modifier parameter is out of range";
     case FA_ERR_WORKSPACE: return "workspace missing or too small";
     case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_SCRATCH: return "problem needs more than fa_bwd_noalloc's fixed device scratch";
     default: return "unknown status";
   }
 }
@@ -274,11 +275,16 @@ size_t fa_bwd_rel_bias_workspace_bytes(int B, int Hq, int Sq, int Skv) {
   return (size_t)B * Hq * (size_t)cdiv(Sq, kTileQ) * ((size_t)Skv + kBiasRowPad) * sizeof(float);
 }
 
-int fa_bwd_phase(int phase, const void* q, const void* k, const void* v, const void* out, const void* dout,
-                 const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes, int B, int Hq,
-                 int Hkv, int Sq, int Skv, int D, int dtype, float scale, int mask_kind,
-                 const fa_mask_params* mask_params, int score_mod_kind, const fa_mod_params* mod_params,
-                 const fa_block_mask* block_mask, void* stream) {
+}  // extern "C"
+
+// The backward entry points.  workspace == nullptr with use_scratch: the
+// workspace is the library's fixed device array (fa_bwd_noalloc), whose
+// address is looked up only after every argument has passed validation.
+static int bwd_entry(int phase, const void* q, const void* k, const void* v, const void* out, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                     bool use_scratch, int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype, float scale,
+                     int mask_kind, const fa_mask_params* mask_params, int score_mod_kind,
+                     const fa_mod_params* mod_params, const fa_block_mask* block_mask, void* stream) {
   if (phase <= 0 || (phase & ~(FA_BWD_DELTA | FA_BWD_DKDV | FA_BWD_DQ)) != 0) return FA_ERR_PARAM;
   if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   int rc = check_shapes(B, Hq, Hkv, Sq, Skv, D);
@@ -296,8 +302,12 @@ int fa_bwd_phase(int phase, const void* q, const void* k, const void* v, const v
   if (has_q) {
     if (!lse) return FA_ERR_NULL;
     if (!aligned(lse, 4)) return FA_ERR_ALIGN;
-    if (!workspace || ws_bytes < fa_bwd_workspace_bytes(B, Hq, Sq, D)) return FA_ERR_WORKSPACE;
-    if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
+    if (use_scratch) {
+      if (fa_bwd_workspace_bytes(B, Hq, Sq, D) > kScratchBytes) return FA_ERR_SCRATCH;
+    } else {
+      if (!workspace || ws_bytes < fa_bwd_workspace_bytes(B, Hq, Sq, D)) return FA_ERR_WORKSPACE;
+      if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
+    }
   }
   // Relative-bias gradient: output table and the per-tile scratch.
   const bool bias_grad = score_mod_kind == FA_MOD_REL_BIAS && mod_params->rel_bias_grad != nullptr &&
@@ -314,6 +324,7 @@ int fa_bwd_phase(int phase, const void* q, const void* k, const void* v, const v
     a.mod.rel_bias_grad = mod_params->rel_bias_grad;
   }
   if (B == 0 && !bias_grad) return FA_OK;
+  if (use_scratch && scratch_address(&workspace) != hipSuccess) return FA_ERR_LAUNCH;
 
   a.q = q;
   a.k = k;
@@ -343,6 +354,17 @@ int fa_bwd_phase(int phase, const void* q, const void* k, const void* v, const v
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+extern "C" {
+
+int fa_bwd_phase(int phase, const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes, int B, int Hq,
+                 int Hkv, int Sq, int Skv, int D, int dtype, float scale, int mask_kind,
+                 const fa_mask_params* mask_params, int score_mod_kind, const fa_mod_params* mod_params,
+                 const fa_block_mask* block_mask, void* stream) {
+  return bwd_entry(phase, q, k, v, out, dout, lse, dq, dk, dv, workspace, ws_bytes, false, B, Hq, Hkv, Sq, Skv, D,
+                   dtype, scale, mask_kind, mask_params, score_mod_kind, mod_params, block_mask, stream);
+}
+
 int fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
            void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes, int B, int Hq, int Hkv, int Sq, int Skv,
            int D, int dtype, float scale, int mask_kind, const fa_mask_params* mask_params, int score_mod_kind,
@@ -351,6 +373,16 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const v
                       ws_bytes, B, Hq, Hkv, Sq, Skv, D, dtype, scale, mask_kind, mask_params, score_mod_kind,
                       mod_params, block_mask, stream);
 }
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Skv, int D, int dtype,
+                   float scale, int mask_kind, const fa_mask_params* mask_params, int score_mod_kind,
+                   const fa_mod_params* mod_params, const fa_block_mask* block_mask, void* stream) {
+  return bwd_entry(FA_BWD_DELTA | FA_BWD_DKDV | FA_BWD_DQ, q, k, v, out, dout, lse, dq, dk, dv, nullptr, 0, true, B,
+                   Hq, Hkv, Sq, Skv, D, dtype, scale, mask_kind, mask_params, score_mod_kind, mod_params, block_mask,
+                   stream);
+}
+
 
 // Sizes of the block-mask arrays in fa_block_mask_layout's order; false for
 // invalid arguments.

@@ -2,6 +2,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
+#include "../../include/libmiattn.h"
 #include "fa_args.h"
 
 namespace miattn {
@@ -19,6 +20,15 @@ hipError_t launch_block_mask(int mask_kind, int window, const int32_t* doc_ids, 
 hipError_t launch_fp8_fwd(const Fp8FwdArgs& a, int mask, hipStream_t st);
 hipError_t launch_fp8_quantize(const void* x, void* x8, uint8_t* scales, int rows, int S, int D, const float* signs,
                                hipStream_t st);
+
+// Size of the library's fixed device scratch (fa_scratch.hip): the backward
+// workspace of fa_bwd_noalloc, two [B][Hq][Sq] float arrays, i.e. up to
+// 2^21 query rows (B * Hq * Sq).
+constexpr size_t kScratchBytes = FA_NOALLOC_SCRATCH_BYTES;
+
+// Device address of the current device's copy of the scratch array, looked
+// up once per device (the first call with that device current) and cached.
+hipError_t scratch_address(void** ptr);
 
 // Keys per forward step for each instantiation.
 constexpr int fwd_kv_step(bool f32) { return f32 ? 32 : 64; }
