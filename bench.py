@@ -246,6 +246,9 @@ def main():
                          "process per host core (up to --oracle-procs), print one JSON line, no GPU work")
     ap.add_argument("--oracle-procs", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--schedule", choices=["static", "persistent"], default="static",
+                    help="persistent: the forward takes its query tiles from a work queue "
+                         "(fa_mask_params.work_queue)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times) and exit: the reference for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -297,6 +300,7 @@ def main():
     ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.Hq, w.S, w.D), dtype=torch.uint8, device=dev)
     use_bm = w.mask == fa.MASK_DOCUMENT
     bm = fa.build_block_mask(w.mask, w.B, w.S, w.S, window=w.window, doc_ids=doc) if use_bm else None
+    wq = fa.new_work_queue(dev) if args.schedule == "persistent" else None
 
     names = (["block_mask"] if use_bm else []) + ["fwd"] + (["bwd_delta", "bwd_dkdv", "bwd_dq"] if w.backward else [])
     is_fp8 = w.dtype == "fp8"
@@ -324,7 +328,7 @@ def main():
             i += 1
             if evs:
                 evs[i].record(stream)
-        fa.forward(q, k, v, out=out, lse=lse, return_lse=w.lse or w.backward, block_mask=bm, **kw)
+        fa.forward(q, k, v, out=out, lse=lse, return_lse=w.lse or w.backward, block_mask=bm, work_queue=wq, **kw)
         i += 1
         if evs:
             evs[i].record(stream)
@@ -380,7 +384,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D,
                    "mask": MASK_NAMES[w.mask], "mod": MOD_NAMES[w.mod], "window": w.window,
                    "pass": "fwd+bwd" if w.backward else "fwd", "lse": bool(w.lse or w.backward),
-                   "admissible_pairs": npairs},
+                   "admissible_pairs": npairs, "schedule": args.schedule},
         "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         **({"pct_of_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2)} if is_fp8 else {}),
         "fwd_tflops": round(f_fwd / (kernel_ms["fwd"] * 1e-3) / 1e12, 2),

@@ -93,7 +93,21 @@ typedef struct {
                               [B][Hq][ceil(Sq/128)]: fa_fwd ADDS the number of
                               key steps (of fa_fwd_kv_step() columns) each
                               128-row query tile processed.  NULL in production. */
+  int32_t* work_queue;     /* optional, device int32[FA_WORK_QUEUE_INTS], all
+                              zero before its first use.  fa_fwd then runs a
+                              persistent, dynamically scheduled kernel whose
+                              workgroups take query tiles from these counters
+                              (one per XCD, longest tiles first, leftovers
+                              shared) until none is left; the last workgroup
+                              zeroes them again, so repeated calls and graph
+                              replays need no clearing.  Calls that overlap in
+                              time need separate arrays.  Results are
+                              bit-identical to the static schedule's.  NULL:
+                              the static schedule.  Ignored by fa_bwd. */
 } fa_mask_params;
+
+/* Length of fa_mask_params.work_queue. */
+#define FA_WORK_QUEUE_INTS 288
 
 typedef struct {
   const float* alibi_slopes; /* device float [Hq]; NULL: 2^(-8(h+1)/Hq) */

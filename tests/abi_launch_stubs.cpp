@@ -32,5 +32,6 @@ hipError_t launch_fp8_quantize(const void*, void*, uint8_t*, int, int, int, cons
   return hipErrorLaunchFailure;
 }
 hipError_t scratch_address(void**) { return hipErrorNotSupported; }
+hipError_t device_cu_count(int*) { return hipErrorNotSupported; }
 
 }  // namespace miattn

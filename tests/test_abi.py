@@ -83,6 +83,10 @@ def test_fwd_rejects_bad_shapes():
     assert fwd(Sq=1 << 23) == fa.FA_ERR_SHAPE
 
 
+def test_fwd_rejects_misaligned_work_queue():
+    assert fwd(mp=fa.FaMaskParams(0, None, None, 0x100002)) == fa.FA_ERR_ALIGN
+
+
 def test_fwd_rejects_bad_pointers():
     assert fwd(q=None) == fa.FA_ERR_NULL
     assert fwd(o=None) == fa.FA_ERR_NULL

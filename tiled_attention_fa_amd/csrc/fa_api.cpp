@@ -176,7 +176,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, i
   if (lse && !aligned(lse, 4)) return FA_ERR_ALIGN;
   int32_t* visited = mask_params ? mask_params->visited : nullptr;
   if (visited && !aligned(visited, 4)) return FA_ERR_ALIGN;
+  int32_t* queue = mask_params ? mask_params->work_queue : nullptr;
+  if (queue && !aligned(queue, 4)) return FA_ERR_ALIGN;
   if (!has_q) return FA_OK;
+  if (queue && device_cu_count(&a.n_cu) != hipSuccess) return FA_ERR_LAUNCH;
+  a.queue = queue;
 
   a.q = q;
   a.k = k;

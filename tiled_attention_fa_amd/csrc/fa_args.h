@@ -63,6 +63,8 @@ struct FwdArgs {
   MaskArgs mask;
   ModArgs mod;
   BlockMaskArgs bm;
+  int32_t* queue;  // null: static schedule; else the work queue of a persistent launch
+  int n_cu;        // compute units of the device (persistent grid size)
 };
 
 // FP8 forward: E4M3 tensors with one E8M0 scale byte per 128-row block of

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/libmiattn.h"
 #include "fa_args.h"
 
 namespace miattn {
@@ -245,6 +246,83 @@ __device__ __forceinline__ void decode_work(int P, int B, int Hq, int Hkv, int n
     hq = hh - b * Hq;
   }
   tile = heavy_first ? (n_tiles - 1 - r) : r;
+}
+
+// ---------------------------------------------------------------- work queue
+// Persistent kernels take the static schedule's workgroup indices P from a
+// queue of counters in caller memory (int32[kQueueInts], zero at launch).
+// When the (batch, kv-head) units pin to XCDs (decode_work), there is one
+// counter per XCD over P = 8 i + x; otherwise one counter over P = i.  A last
+// counter counts finished workgroups; the last to finish zeroes them all.
+// Each counter has a 128-byte line of its own.
+constexpr int kXcds = 8;
+constexpr int kQueueStride = 32;                   // ints per counter
+constexpr int kQueueInts = (kXcds + 1) * kQueueStride;
+constexpr int kQueueDone = kXcds * kQueueStride;   // the finished-workgroup count
+
+static_assert(kQueueInts == FA_WORK_QUEUE_INTS, "the header states the queue length");
+
+struct WorkQueue {
+  int n_queues;   // 8 (XCD-pinned) or 1
+  int per_queue;  // workgroup indices per counter
+};
+
+__device__ __forceinline__ WorkQueue work_queue_shape(int B, int Hq, int Hkv, int n_tiles) {
+  const int NU = B * Hkv;
+  if ((NU & 7) == 0) return WorkQueue{kXcds, (NU >> 3) * (Hq / Hkv) * n_tiles};
+  return WorkQueue{1, B * Hq * n_tiles};
+}
+
+__device__ __forceinline__ int queue_home(const WorkQueue& wq, int home) { return wq.n_queues == 1 ? 0 : home; }
+
+// Raw index from the workgroup's own counter (one device-scope atomic; the
+// caller may issue it early and consume the result later).
+__device__ __forceinline__ int take_home(int32_t* q, const WorkQueue& wq, int home) {
+  return __hip_atomic_fetch_add(q + queue_home(wq, home) * kQueueStride, 1, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The workgroup's next index P, or -1 once every counter is past its end.
+// Thread 0 decides: `i_home` is an index already taken from the own counter
+// (or -1 if none was taken); when it is past the end, the other counters are
+// tried in turn.  The workgroup reads the result through `slot`.  Counters
+// only grow, so every workgroup ends.
+__device__ __forceinline__ int finish_pull(int32_t* q, const WorkQueue& wq, int home, int i_home, int* slot) {
+  if (threadIdx.x == 0) {
+    int P = -1;
+    if (i_home < 0) i_home = take_home(q, wq, home);
+    if (i_home < wq.per_queue) {
+      P = i_home * wq.n_queues + queue_home(wq, home);
+    } else {
+      for (int k = 1; k < wq.n_queues; ++k) {
+        int32_t* c = q + ((home + k) & (kXcds - 1)) * kQueueStride;
+        if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= wq.per_queue) continue;
+        const int i = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (i < wq.per_queue) {
+          P = i * wq.n_queues + ((home + k) & (kXcds - 1));
+          break;
+        }
+      }
+    }
+    *slot = P;
+  }
+  __syncthreads();
+  const int P = *slot;
+  __syncthreads();  // the slot is rewritten by the next pull
+  return P;
+}
+
+// End of a persistent workgroup: count it as finished; the last one zeroes
+// the queue (every other workgroup has made its last pull by then), so the
+// next launch, or a graph replay, starts from zero without a clearing pass.
+__device__ __forceinline__ void release_queue(int32_t* q) {
+  if (threadIdx.x == 0) {
+    const int done = __hip_atomic_fetch_add(q + kQueueDone, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == (int)gridDim.x - 1) {
+      for (int x = 0; x <= kXcds; ++x)
+        __hip_atomic_store(q + x * kQueueStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 // Running row sum with compensation (Kahan): l is the sum, c the negated

@@ -161,8 +161,14 @@ struct FwdSmem {
   static constexpr int TILE = FwdCfg<F32>::BN * ROW;     // one K or V tile
 };
 
-template <int D, bool F32, int MASK, int MOD, bool BM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(FwdArgs a) {
+// One 128-row query tile (b, hq, qt) of the 4-wave forward: the whole
+// online-softmax pass over its key steps and the epilogue.  Every wave of the
+// workgroup calls it; on return every read of the LDS stages has finished.
+// `at_last_step` runs at the start of the tile's last key step, after that
+// step's loads are issued (persistent kernels take their next tile there, so
+// the queue's latency hides behind the step).
+template <int D, bool F32, int MASK, int MOD, bool BM, typename AtLast>
+__device__ __forceinline__ void fwd_tile(const FwdArgs& a, int b, int hq, int qt, AtLast at_last_step) {
   using Cfg = FwdCfg<F32>;
   using Sm = FwdSmem<D, F32>;
   constexpr int BN = Cfg::BN, NT = Cfg::NT;
@@ -183,10 +189,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int NB = (kTileQ + BN + 62) / 64 * 64;
   __shared__ __attribute__((aligned(16))) float sB0[REL ? NB : 1], sB1[REL && !F32 ? NB : 1];
 
-  int b, hq, qt;
-  decode_work(blockIdx.x, a.B, a.Hq, a.Hkv, a.n_qt,
-              (MASK == MASK_CAUSAL || MASK == MASK_DOCUMENT) && !(BM && a.bm.q_order), b, hq, qt);
-  if constexpr (BM) qt = ordered_tile(a.bm.q_order, a.bm.n_b, b, a.bm.n_q, qt, qt);
   const int hk = hq / a.G;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wave = wave_uniform(tid >> 6);  // uniform: per-wave branches stay scalar
@@ -333,6 +335,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int blk_nn = fetch_blk(s + 2);
     if constexpr (BM) st_n = have_next ? bm_state[blk_n] : 0;
     if (k0 < Skv) ++visited;
+    if (!have_next) at_last_step();
 
     int cls;
     if constexpr (BM) {
@@ -545,6 +548,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       a.lse[(size_t)(b * a.Hq + hq) * Sq + qi] = lt > 0.0f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 + lse_shift : kNegInf;
   }
   if (a.visited != nullptr && tid == 0) atomicAdd(&a.visited[(size_t)(b * a.Hq + hq) * a.n_qt + qt], visited);
+}
+
+// Query tile of the static schedule's workgroup P: XCD-pinned (batch, kv
+// head) units, heaviest causal tiles first, or the block mask's
+// longest-first order.
+template <int MASK, bool BM>
+__device__ __forceinline__ void fwd_tile_of(const FwdArgs& a, int P, int& b, int& hq, int& qt) {
+  decode_work(P, a.B, a.Hq, a.Hkv, a.n_qt, (MASK == MASK_CAUSAL || MASK == MASK_DOCUMENT) && !(BM && a.bm.q_order),
+              b, hq, qt);
+  if constexpr (BM) qt = ordered_tile(a.bm.q_order, a.bm.n_b, b, a.bm.n_q, qt, qt);
+}
+
+template <int D, bool F32, int MASK, int MOD, bool BM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(FwdArgs a) {
+  int b, hq, qt;
+  fwd_tile_of<MASK, BM>(a, blockIdx.x, b, hq, qt);
+  fwd_tile<D, F32, MASK, MOD, BM>(a, b, hq, qt, [] {});
+}
+
+// Persistent, dynamically scheduled form of fwd_kernel (the role of a
+// hardware tile scheduler with persistent workgroups on the "PyTorch
+// FlexAttention, FlashAttention-4" page, 섹션별 상세, and the persistent
+// scheduling of the "FlashInfer SM120" page, §4): about two workgroups per
+// compute unit, each taking query tiles from a work queue in caller memory
+// until it is empty.  The queue holds one counter per XCD over that XCD's
+// share of the static schedule (its (batch, kv-head) units, longest tiles
+// first); a workgroup drains its own XCD's counter, keeping K/V in that L2,
+// then takes leftovers from the others.  Results are those of fwd_kernel,
+// bit for bit: the same per-tile code runs, only the order of tiles differs.
+template <int D, bool F32, int MASK, int MOD, bool BM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_persist_kernel(FwdArgs a) {
+  __shared__ int sUnit;
+  const WorkQueue wq = work_queue_shape(a.B, a.Hq, a.Hkv, a.n_qt);
+  const int home = (int)(blockIdx.x % kXcds);
+  int P = finish_pull(a.queue, wq, home, -1, &sUnit);
+  while (P >= 0) {
+    int b, hq, qt;
+    fwd_tile_of<MASK, BM>(a, P, b, hq, qt);
+    // The next tile's index is taken (thread 0) when this tile's last step
+    // starts and read after the tile, when the step's loads have landed.
+    int i_next = -1;
+    fwd_tile<D, F32, MASK, MOD, BM>(a, b, hq, qt, [&] {
+      if (threadIdx.x == 0) i_next = take_home(a.queue, wq, home);
+    });
+    P = finish_pull(a.queue, wq, home, i_next, &sUnit);
+  }
+  release_queue(a.queue);
 }
 
 // ---------------------------------------------------------------- ping-pong forward
@@ -800,15 +850,26 @@ static hipError_t launch_pp(const FwdArgs& a, int mod, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int D, bool F32, int MASK, bool BM, int MOD>
+static void launch_one(const FwdArgs& a, hipStream_t st) {
+  const int tiles = a.B * a.Hq * a.n_qt;
+  if (a.queue != nullptr) {
+    // Two workgroups per compute unit, but no more than there are tiles.
+    const int grid = min(tiles, 2 * a.n_cu);
+    hipLaunchKernelGGL((fwd_persist_kernel<D, F32, MASK, MOD, BM>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((fwd_kernel<D, F32, MASK, MOD, BM>), dim3((unsigned)tiles), dim3(256), 0, st, a);
+  }
+}
+
 template <int D, bool F32, int MASK, bool BM>
 static hipError_t launch_mod(const FwdArgs& a, int mod, hipStream_t st) {
-  const dim3 grid((unsigned)(a.B * a.Hq * a.n_qt)), block(256);
   switch (mod) {
-    case MOD_NONE: hipLaunchKernelGGL((fwd_kernel<D, F32, MASK, MOD_NONE, BM>), grid, block, 0, st, a); break;
-    case MOD_ALIBI: hipLaunchKernelGGL((fwd_kernel<D, F32, MASK, MOD_ALIBI, BM>), grid, block, 0, st, a); break;
-    case MOD_SOFTCAP: hipLaunchKernelGGL((fwd_kernel<D, F32, MASK, MOD_SOFTCAP, BM>), grid, block, 0, st, a); break;
-    case MOD_REL_BIAS: hipLaunchKernelGGL((fwd_kernel<D, F32, MASK, MOD_REL_BIAS, BM>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((fwd_kernel<D, F32, MASK, MOD_BOOST, BM>), grid, block, 0, st, a); break;
+    case MOD_NONE: launch_one<D, F32, MASK, BM, MOD_NONE>(a, st); break;
+    case MOD_ALIBI: launch_one<D, F32, MASK, BM, MOD_ALIBI>(a, st); break;
+    case MOD_SOFTCAP: launch_one<D, F32, MASK, BM, MOD_SOFTCAP>(a, st); break;
+    case MOD_REL_BIAS: launch_one<D, F32, MASK, BM, MOD_REL_BIAS>(a, st); break;
+    default: launch_one<D, F32, MASK, BM, MOD_BOOST>(a, st); break;
   }
   return hipGetLastError();
 }
@@ -825,7 +886,8 @@ static hipError_t launch_bm(const FwdArgs& a, int mod, hipStream_t st) {
   // epilogue behind the other's steps: causal B16 H16 S1024 0.123 against
   // 0.134 ms (equal at S = 2048, the ping-pong kernel 3-5 % ahead from 4096).
   if constexpr (!F32 && MASK != MASK_DOCUMENT) {
-    if (a.Skv > 1024 && (MASK != MASK_WINDOW || a.mask.window > 2048)) return launch_pp<D, MASK>(a, mod, st);
+    if (a.queue == nullptr && a.Skv > 1024 && (MASK != MASK_WINDOW || a.mask.window > 2048))
+      return launch_pp<D, MASK>(a, mod, st);
   }
   return launch_mod<D, F32, MASK, false>(a, mod, st);
 }

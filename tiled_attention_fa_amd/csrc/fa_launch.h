@@ -30,6 +30,10 @@ constexpr size_t kScratchBytes = FA_NOALLOC_SCRATCH_BYTES;
 // up once per device (the first call with that device current) and cached.
 hipError_t scratch_address(void** ptr);
 
+// Compute units of the current device (the size of persistent grids),
+// looked up once per device and cached.
+hipError_t device_cu_count(int* n);
+
 // Keys per forward step for each instantiation.
 constexpr int fwd_kv_step(bool f32) { return f32 ? 32 : 64; }
 
