@@ -219,22 +219,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const float slope = head_slope<MOD>(a.mod, hq, a.Hq);
       const int ch = 2 * g16 + ((gi & 3) >> 1);
       const int half = (gi & 1) * 8;
+      // LDS operand offsets, rebuilt each step from two bases (XOR on the
+      // chunk index, row_base) rather than held as one register per chunk:
+      // row reads of chunk 2c + hh of row l32 (Q, dO; the V rows of this wave
+      // share them, 32 rows further per wave), and transposing reads of rows
+      // 16 cc + r00 (+ 8), chunk 4 dt + ch, at (t ^ 64 dt) + 16 cc ROW.
+      const int qrow = opaque(row_base<D>(l32) ^ (16 * hh));
+      const char* vw = sV + 32 * wave * ROW;
       f32x16 sp = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        sp = mfma_bf16(*(const u32x4*)(qs + l32 * ROW + swz<D>(l32, 2 * c + hh) * 16), kf[c], sp);
-        dp = mfma_bf16(*(const u32x4*)(ds + l32 * ROW + swz<D>(l32, 2 * c + hh) * 16),
-                       *(const u32x4*)(sV + vrow * ROW + swz<D>(vrow, 2 * c + hh) * 16), dp);
+        const int o = qrow ^ (32 * c);
+        sp = mfma_bf16(*(const u32x4*)(qs + o), kf[c], sp);
+        dp = mfma_bf16(*(const u32x4*)(ds + o), *(const u32x4*)(vw + o), dp);
       }
       // P and dS (register r: query q0 + 8(r/4) + 4hh + r%4).  Full tiles
       // take a branch without the mask test.  bl[8 rq + e] is the bias of
       // query q0 + 8 rq + 4hh + e and this lane's key.
       const float* bl = bs + (BK - 1 - 32 * wave - l32 + 4 * hh);
+      // Row offsets 8 rq + 4 hh + e are rebuilt from this each step rather
+      // than kept in 16 registers across the loop.
+      const int hh4 = opaque(4 * hh);
       auto pds = [&](auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
-          const int ir = 8 * rq + 4 * hh;
+          const int ir = 8 * rq + hh4;
           const f32x4 L4 = *(const f32x4*)&ls[ir];
           const f32x4 E4 = *(const f32x4*)&es[ir];
 #pragma unroll
@@ -260,13 +270,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       const u32x4 pb0 = pack8(sp, 0), pb1 = pack8(sp, 8);
       const u32x4 sb0 = pack8(dp, 0), sb1 = pack8(dp, 8);
+      const int r00 = 4 * hh + (gi >> 2);
+      const int t0 = opaque((row_base<D>(r00) | half) ^ (16 * ch));
+      const int t1 = opaque((row_base<D>(r00 + 8) | half) ^ (16 * ch));
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-          const int r0 = 16 * cc + 4 * hh + (gi >> 2), r1 = r0 + 8;
-          const int o0 = r0 * ROW + swz<D>(r0, 4 * dt + ch) * 16 + half;
-          const int o1 = r1 * ROW + swz<D>(r1, 4 * dt + ch) * 16 + half;
+          const int o0 = (t0 ^ (64 * dt)) + 16 * cc * ROW;
+          const int o1 = (t1 ^ (64 * dt)) + 16 * cc * ROW;
           const u32x2 dlo = lds_read_tr16(ds + o0), dhi = lds_read_tr16(ds + o1);
           dv[dt] = mfma_bf16(u32x4{dlo[0], dlo[1], dhi[0], dhi[1]}, cc ? pb1 : pb0, dv[dt]);
           const u32x2 qlo = lds_read_tr16(qs + o0), qhi = lds_read_tr16(qs + o1);
@@ -492,15 +504,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // in this (wave, half-wave) slice (c = 32t + 8(r/4) + r%4).
       const float* bl = bs + (32 * wave + l32 + 4 - 4 * hh);
       float* gl = gs + (2 * wave + hh) * GS + (l32 + 4 - 4 * hh);
+      // LDS operand offsets, rebuilt each step from a few bases (XOR on the
+      // chunk index, row_base) rather than held as one register per chunk:
+      // row reads of chunk 2c + hh of row 32t + l32 (K, V), and transposing
+      // reads of rows 32t + 16cc + r00 (+ 8), chunk 4dt + ch, of K.
+      const int krow = opaque(row_base<D>(l32) ^ (16 * hh));
+      const int r00 = 4 * hh + (gi >> 2);
+      const int t0 = opaque((row_base<D>(r00) | half) ^ (16 * ch));
+      const int t1 = opaque((row_base<D>(r00 + 8) | half) ^ (16 * ch));
       // One 32-key subtile at a time keeps the live registers low.
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         f32x16 st = f32x16{}, dpt = f32x16{};
-        const int r = 32 * t + l32;
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-          st = mfma_bf16(*(const u32x4*)(ks + r * ROW + swz<D>(r, 2 * c + hh) * 16), qf[c], st);
-          dpt = mfma_bf16(*(const u32x4*)(vs + r * ROW + swz<D>(r, 2 * c + hh) * 16), of[c], dpt);
+          const int o = (krow ^ (32 * c)) + 32 * t * ROW;
+          st = mfma_bf16(*(const u32x4*)(ks + o), qf[c], st);
+          dpt = mfma_bf16(*(const u32x4*)(vs + o), of[c], dpt);
         }
         // Full tiles take a branch without the mask test.
         auto pds = [&](auto masked) {
@@ -534,9 +554,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
           for (int cc = 0; cc < 2; ++cc) {
-            const int r0 = 32 * t + 16 * cc + 4 * hh + (gi >> 2), r1 = r0 + 8;
-            const u32x2 lo = lds_read_tr16(ks + r0 * ROW + swz<D>(r0, 4 * dt + ch) * 16 + half);
-            const u32x2 hi = lds_read_tr16(ks + r1 * ROW + swz<D>(r1, 4 * dt + ch) * 16 + half);
+            const int rows = (32 * t + 16 * cc) * ROW;
+            const u32x2 lo = lds_read_tr16(ks + ((t0 ^ (64 * dt)) + rows));
+            const u32x2 hi = lds_read_tr16(ks + ((t1 ^ (64 * dt)) + rows));
             dq[dt] = mfma_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, cc ? sb1 : sb0, dq[dt]);
           }
       }

@@ -40,6 +40,15 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
 // in a device function so kernel bodies name no target builtin directly.
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// x, hidden from the optimizer (an empty asm that claims to modify it):
+// values derived from it are recomputed where they are used, inside the loop
+// that calls this, instead of being hoisted out of the loop, each into a
+// register of its own.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
@@ -86,6 +95,14 @@ template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
   if constexpr (D == 128) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
   return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// Byte offset of chunk 0 of swizzled row r.  Because the swizzle is an XOR
+// on the chunk index, and chunk bits (4 .. log2(ROW) - 1) never carry into
+// the row bits, chunk c of row r sits at row_base(r) ^ (16 c).
+template <int D>
+__device__ __forceinline__ int row_base(int r) {
+  return r * (2 * D) + swz<D>(r, 0) * 16;
 }
 
 // ---------------------------------------------------------------- global -> LDS
