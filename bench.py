@@ -246,6 +246,9 @@ def main():
                          "process per host core (up to --oracle-procs), print one JSON line, no GPU work")
     ap.add_argument("--oracle-procs", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bwd-dq", choices=["stored", "recompute"], default="recompute",
+                    help="stored: the backward workspace has room for dS (fa_bwd_ds_workspace_bytes) where the "
+                         "mask allows, so the dQ launch reads dS instead of recomputing it")
     ap.add_argument("--schedule", choices=["static", "persistent"], default="static",
                     help="persistent: the forward takes its query tiles from a work queue "
                          "(fa_mask_params.work_queue)")
@@ -297,7 +300,10 @@ def main():
     out = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
     grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)) if w.backward else None
-    ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.Hq, w.S, w.D), dtype=torch.uint8, device=dev)
+    ws_bytes = fa.fa_bwd_workspace_bytes(w.B, w.Hq, w.S, w.D)
+    if w.backward and args.bwd_dq == "stored":
+        ws_bytes = max(ws_bytes, fa.fa_bwd_ds_workspace_bytes(w.B, w.Hq, w.S, w.S, w.D, w.mask))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     use_bm = w.mask == fa.MASK_DOCUMENT
     bm = fa.build_block_mask(w.mask, w.B, w.S, w.S, window=w.window, doc_ids=doc) if use_bm else None
     wq = fa.new_work_queue(dev) if args.schedule == "persistent" else None
@@ -384,7 +390,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D,
                    "mask": MASK_NAMES[w.mask], "mod": MOD_NAMES[w.mod], "window": w.window,
                    "pass": "fwd+bwd" if w.backward else "fwd", "lse": bool(w.lse or w.backward),
-                   "admissible_pairs": npairs, "schedule": args.schedule},
+                   "admissible_pairs": npairs, "schedule": args.schedule,
+                   **({"bwd_dq": args.bwd_dq, "workspace_bytes": ws_bytes} if w.backward else {})},
         "pct_of_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         **({"pct_of_fp8_peak": round(100.0 * tflops / PEAK_FP8_TFLOPS, 2)} if is_fp8 else {}),
         "fwd_tflops": round(f_fwd / (kernel_ms["fwd"] * 1e-3) / 1e12, 2),

@@ -198,9 +198,11 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const v
 
 /* The three launches of fa_bwd, one at a time: FA_BWD_DELTA writes
  * rowsum(dout * out) into the workspace; FA_BWD_DKDV writes dk and dv;
- * FA_BWD_DQ writes dq.  Same arguments and validation as fa_bwd.  DKDV and
- * DQ only read what DELTA wrote, so once DELTA has finished they may run
- * concurrently on different streams.  Calling the three in order on one
+ * FA_BWD_DQ writes dq.  Same arguments and validation as fa_bwd.  With a
+ * workspace of fa_bwd_workspace_bytes, DKDV and DQ only read what DELTA
+ * wrote, so once DELTA has finished they may run concurrently on different
+ * streams; with the stored-dS workspace (fa_bwd_ds_workspace_bytes) DQ reads
+ * what DKDV wrote and must follow it.  Calling the three in order on one
  * stream is exactly fa_bwd. */
 enum { FA_BWD_DELTA = 1, FA_BWD_DKDV = 2, FA_BWD_DQ = 4 };
 int fa_bwd_phase(int phase, const void* q, const void* k, const void* v, const void* out,
@@ -211,6 +213,20 @@ int fa_bwd_phase(int phase, const void* q, const void* k, const void* v, const v
                  const fa_block_mask* block_mask, void* stream);
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq, int D);
+
+/* Workspace size of the stored-dS backward: fa_bwd_workspace_bytes plus room
+ * for the bf16 dS tiles the dK/dV phase computes anyway (2 bytes per query-
+ * key pair it visits: B * Hq * Sq * Skv * 2 without a mask, about half that
+ * under the causal mask; 2.2 GB at B=2, Hq=16, S=8192 causal).  Given a
+ * workspace at least this large, fa_bwd / fa_bwd_phase store dS in the DKDV
+ * phase and the DQ phase computes dQ = scale dS K from it instead of
+ * recomputing the scores and dO V^T (FA_MASK_NONE or FA_MASK_CAUSAL, no block
+ * mask, any modifier but FA_MOD_REL_BIAS; other calls ignore the extra
+ * space).  Then DQ reads what DKDV wrote, so DQ must run after DKDV.  Results
+ * meet the same bars as the recomputing path (not the same bits: dS comes
+ * from the other kernel's accumulation order) and are deterministic.
+ * Returns 0 for other mask kinds or invalid sizes. */
+size_t fa_bwd_ds_workspace_bytes(int B, int Hq, int Sq, int Skv, int D, int mask_kind);
 
 /* Size of the fixed device scratch of fa_bwd_noalloc: 16 MiB per GPU, which
  * holds the backward workspace of up to B * Hq * Sq = 2^21 query rows. */

@@ -28,6 +28,7 @@ BLOCK = 128
 FA_BWD_DELTA, FA_BWD_DKDV, FA_BWD_DQ = 1, 2, 4
 
 EXPORTED = ("fa_fwd", "fa_fwd_kv_step", "fa_bwd", "fa_bwd_phase", "fa_bwd_noalloc", "fa_bwd_workspace_bytes",
+            "fa_bwd_ds_workspace_bytes",
             "fa_bwd_rel_bias_workspace_bytes",
             "fa_block_mask_bytes", "fa_block_mask_layout", "fa_block_mask_build", "fa_fp8_quantize", "fa_fwd_fp8",
             "fa_status_str", "fa_version")
@@ -93,6 +94,8 @@ def declare_prototypes(L: ctypes.CDLL) -> ctypes.CDLL:
     L.fa_bwd_noalloc.restype = _I
     L.fa_bwd_workspace_bytes.argtypes = [_I, _I, _I, _I]
     L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.fa_bwd_ds_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
+    L.fa_bwd_ds_workspace_bytes.restype = ctypes.c_size_t
     L.fa_bwd_rel_bias_workspace_bytes.argtypes = [_I, _I, _I, _I]
     L.fa_bwd_rel_bias_workspace_bytes.restype = ctypes.c_size_t
     L.fa_block_mask_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
@@ -140,6 +143,10 @@ def fa_block_mask_build(*args) -> int:
 
 def fa_bwd_workspace_bytes(B: int, Hq: int, Sq: int, D: int) -> int:
     return int(lib().fa_bwd_workspace_bytes(B, Hq, Sq, D))
+
+
+def fa_bwd_ds_workspace_bytes(B: int, Hq: int, Sq: int, Skv: int, D: int, mask: int) -> int:
+    return int(lib().fa_bwd_ds_workspace_bytes(B, Hq, Sq, Skv, D, mask))
 
 
 def fa_bwd_rel_bias_workspace_bytes(B: int, Hq: int, Sq: int, Skv: int) -> int:
@@ -402,13 +409,16 @@ def backward(q, k, v, out, dout, lse, *, scale=None, mask=MASK_NONE, window=0, d
              mod=MOD_NONE, alibi_slopes=None, softcap=0.0, boost_radius=0, boost_factor=1.0,
              rel_bias=None, rel_bias_grad=None, rel_bias_ws=None,
              block_mask=None, workspace=None, grads=None, stream=None,
-             phases=FA_BWD_DELTA | FA_BWD_DKDV | FA_BWD_DQ, noalloc=False):
+             phases=FA_BWD_DELTA | FA_BWD_DKDV | FA_BWD_DQ, noalloc=False, store_ds=False):
     """(dq, dk, dv) of sum(O * dout), recomputing P from ``lse``.
 
     ``phases`` selects which of the three backward launches run (all by
     default, which is fa_bwd).  ``noalloc``: call fa_bwd_noalloc, whose
     workspace is the library's fixed device scratch (all phases; with
-    ``grads`` given and no relative-bias gradient nothing is allocated).  With MOD_REL_BIAS, ``rel_bias_grad`` (float32
+    ``grads`` given and no relative-bias gradient nothing is allocated).
+    ``store_ds``: allocate the stored-dS workspace (fa_bwd_ds_workspace_bytes)
+    when none is given, so dQ is computed from the dS the dK/dV phase
+    stores (unmasked and causal attention).  With MOD_REL_BIAS, ``rel_bias_grad`` (float32
     [Hq, Sq + Skv - 1], or True to allocate it) receives the gradient of the
     bias table; its scratch ``rel_bias_ws`` is allocated when not given.  The
     return value is then (dq, dk, dv, rel_bias_grad)."""
@@ -430,6 +440,8 @@ def backward(q, k, v, out, dout, lse, *, scale=None, mask=MASK_NONE, window=0, d
             raise ValueError("noalloc: the workspace is the library's own, and every phase runs")
     else:
         ws_bytes = fa_bwd_workspace_bytes(B, Hq, Sq, D)
+        if store_ds:
+            ws_bytes = max(ws_bytes, fa_bwd_ds_workspace_bytes(B, Hq, Sq, Skv, D, mask))
         if workspace is None:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
         _dense(workspace, "workspace", None, None, q.device)

@@ -274,6 +274,20 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq, int D) {
   return 2 * ws_half(B, Hq, Sq);
 }
 
+size_t fa_bwd_ds_workspace_bytes(int B, int Hq, int Sq, int Skv, int D, int mask_kind) {
+  if (B <= 0 || Hq <= 0 || Sq <= 0 || Skv <= 0 || (D != 64 && D != 128)) return 0;
+  if (Sq > kMaxSeq || Skv > kMaxSeq) return 0;
+  const int n_qs = (int)cdiv(Sq, 32), n_kt = (int)cdiv(Skv, kTileQ);
+  long blocks;
+  if (mask_kind == FA_MASK_NONE)
+    blocks = ds_block<MASK_NONE>(n_kt, 0, n_qs);
+  else if (mask_kind == FA_MASK_CAUSAL)
+    blocks = ds_block<MASK_CAUSAL>(n_kt, 4 * n_kt, n_qs);
+  else
+    return 0;
+  return fa_bwd_workspace_bytes(B, Hq, Sq, D) + (size_t)B * Hq * (size_t)blocks * kDsBlock * sizeof(uint16_t);
+}
+
 size_t fa_bwd_rel_bias_workspace_bytes(int B, int Hq, int Sq, int Skv) {
   if (B <= 0 || Hq <= 0 || Sq <= 0 || Skv < 0) return 0;
   return (size_t)B * Hq * (size_t)cdiv(Sq, kTileQ) * ((size_t)Skv + kBiasRowPad) * sizeof(float);
@@ -349,10 +363,23 @@ static int bwd_entry(int phase, const void* q, const void* k, const void* v, con
   a.Skv = Skv;
   a.n_qt = (int)cdiv(Sq, kTileQ);
   a.n_kt = (int)cdiv(Skv, kTileQ);
+  a.n_qs = (int)cdiv(Sq, 32);
   a.scale = scale;
   a.scale_log2 = log2_multiplier(scale);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int mod = kernel_mod(score_mod_kind, a.mod);
+  // Stored dS: a workspace of fa_bwd_ds_workspace_bytes holds the dS tiles
+  // after the row arrays, and the dQ launch reads them instead of
+  // recomputing S and dP (no mask or causal, no block mask, no relative bias).
+  if (!use_scratch && B > 0 && Sq > 0 && Skv > 0 && !block_mask && mod != FA_MOD_REL_BIAS &&
+      (mask_kind == FA_MASK_NONE || mask_kind == FA_MASK_CAUSAL)) {
+    const size_t need = fa_bwd_ds_workspace_bytes(B, Hq, Sq, Skv, D, mask_kind);
+    if (need > 0 && ws_bytes >= need) {
+      a.ds = (uint16_t*)((char*)workspace + 2 * ws_half(B, Hq, Sq));
+      a.ds_blocks = mask_kind == FA_MASK_CAUSAL ? ds_block<MASK_CAUSAL>(a.n_kt, 4 * a.n_kt, a.n_qs)
+                                                : ds_block<MASK_NONE>(a.n_kt, 0, a.n_qs);
+    }
+  }
   const hipError_t e = D == 128 ? launch_bwd_d<128>(a, mask_kind, mod, phase, st)
                                 : launch_bwd_d<64>(a, mask_kind, mod, phase, st);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;

@@ -102,6 +102,31 @@ struct BwdArgs {
   MaskArgs mask;
   ModArgs mod;
   BlockMaskArgs bm;
+  // Stored-dS backward (null: the dQ kernel recomputes S and dP): bf16 dS
+  // tiles written by the dK/dV kernel and read by the dQ kernel, blocks of
+  // 32 query rows x 128 keys (ds_block), ds_blocks per (batch, query head).
+  uint16_t* ds;
+  long ds_blocks;
+  int n_qs;  // query steps of 32 rows
 };
+
+// Elements of one stored dS block: 4 waves x 64 lanes x 16 bf16.
+constexpr int kDsBlock = 4096;
+
+// Index of the stored dS block of key tile kt (128 keys) and query step qs
+// (32 rows) within one (batch, query head), for n_qs query steps.  Without
+// a mask every pair of (kt, qs) has a block; under the causal mask key tile
+// kt has the query steps qs >= 4 kt (the steps the dK/dV kernel visits), and
+// the blocks are packed tile after tile.  ds_block(n_kt, 4 n_kt, n_qs) is
+// the number of blocks per (batch, query head).  (constexpr: host and device.)
+template <int MASK>
+constexpr long ds_block(int kt, int qs, int n_qs) {
+  if constexpr (MASK == MASK_CAUSAL) {
+    const long m = kt < (n_qs + 3) / 4 ? kt : (n_qs + 3) / 4;
+    return m * n_qs - 2 * m * (m - 1) + (qs - 4L * kt);
+  } else {
+    return (long)kt * n_qs + qs;
+  }
+}
 
 }  // namespace miattn

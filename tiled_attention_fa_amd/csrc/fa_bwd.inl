@@ -88,7 +88,11 @@ __device__ __forceinline__ u32x4 pack8(const f32x16& v, int base) {
 // lane, so P and dS are repacked in registers as the B operands of
 // dV^T += dO^T P and dK^T += Q^T dS, whose A operands are transposing LDS
 // reads.  Two workgroups fit per CU (2 waves per SIMD).
-template <int D, int MASK, int MOD, bool BM>
+// DS: also store each step's bf16 dS (32 queries x this wave's 32 keys, in
+// the register layout: lane l holds 16 queries of key kw0 + l % 32) as a
+// 2 KB piece of block ds_block(kt, q0 / 32), zeros where the wave skips the
+// step, for the dQ kernel that reads dS instead of recomputing it.
+template <int D, int MASK, int MOD, bool BM, bool DS = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BK = 128, BQ = 32;
   constexpr int ROW = D * 2, TILE = BQ * ROW;
@@ -214,6 +218,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     if (q0 + BQ > Sq && cls == TILE_FULL) cls = TILE_PARTIAL;
     if (kw0 >= Skv || q0 >= Sq) cls = TILE_EMPTY;
+    u32x4* dsp = nullptr;
+    if constexpr (DS)
+      dsp = (u32x4*)(a.ds + ((size_t)(b * a.Hq + hq) * a.ds_blocks + ds_block<MASK>(kt, q0 / BQ, a.n_qs)) * kDsBlock) +
+            2 * (wave * 64 + lane);
 
     if (cls != TILE_EMPTY) {
       const float slope = head_slope<MOD>(a.mod, hq, a.Hq);
@@ -284,9 +292,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           const u32x2 qlo = lds_read_tr16(qs + o0), qhi = lds_read_tr16(qs + o1);
           dk[dt] = mfma_bf16(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, cc ? sb1 : sb0, dk[dt]);
         }
+      if constexpr (DS) {
+        dsp[0] = sb0;
+        dsp[1] = sb1;
+      }
+    } else if constexpr (DS) {
+      dsp[0] = u32x4{0, 0, 0, 0};
+      dsp[1] = u32x4{0, 0, 0, 0};
     }
-    wait_loads();
-    __syncthreads();
+    if constexpr (DS) {
+      // The next stage's loads (issued at the start of this step) have
+      // landed; this step's two dS stores may still be in flight.
+      wait_loads_not_last2();
+      phase_barrier();
+    } else {
+      wait_loads();
+      __syncthreads();
+    }
     blk_c = blk_n;
     st_c = st_n;
     blk_n = blk_nn;
@@ -611,6 +633,118 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// ---------------------------------------------------------------- dQ from stored dS
+// dQ = scale dS K with dS read back from the blocks the dK/dV kernel stored
+// (no mask or the causal mask, no relative bias): nothing is recomputed.
+// Workgroup: 4 waves own the 128 query rows of (b, hq, qt), wave w the query
+// step 4 qt + w.  Per step of 64 keys, straight into LDS: the K rows
+// (swizzled, as everywhere) and, per wave, its 64 x 32 piece of dS, gathered
+// so that LDS row j holds key j's two 32-byte lane chunks (the 16 queries of
+// half 0, then of half 1): 64-byte rows, which the transposing reads below
+// access without bank conflicts.  dQ^T += K^T dS^T takes both operands from
+// transposing reads with the same key rows, so their k orders agree; the
+// output column of lane l is position p = l % 32 of those rows, i.e. query
+// 8 ((p % 16) / 4) + 4 (p / 16) + p % 4 of the wave's step.
+template <int D, int MASK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_ds_kernel(BwdArgs a) {
+  static_assert(MASK == MASK_NONE || MASK == MASK_CAUSAL, "stored dS covers the unmasked and causal cases");
+  constexpr int BN = 64, ROW = D * 2, TILE = BN * ROW, DT = D / 32;
+  constexpr int SROW = 64, SWAVE = BN * SROW;  // one wave's dS piece: 4 KB
+  __shared__ __attribute__((aligned(16))) char sK0[TILE], sK1[TILE];
+  __shared__ __attribute__((aligned(16))) char sS0[4 * SWAVE], sS1[4 * SWAVE];
+
+  int b, hq, qt;
+  decode_work(blockIdx.x, a.B, a.Hq, a.Hkv, a.n_qt, MASK == MASK_CAUSAL, b, hq, qt);
+  const int hk = hq / a.G;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = wave_uniform(tid >> 6);
+  const int gi = lane & 15, g16 = (lane >> 4) & 1;
+  const int Sq = a.Sq, Skv = a.Skv;
+  const int q0 = qt * kTileQ, qw0 = q0 + 32 * wave;
+  const bool wave_ok = qw0 < Sq;  // steps past Sq were never stored
+  const int qs = qw0 / 32;
+
+  const uint16_t* K = uniform_ptr((const uint16_t*)a.k + (size_t)(b * a.Hkv + hk) * Skv * D);
+  const uint16_t* dsh = uniform_ptr(a.ds + (size_t)(b * a.Hq + hq) * a.ds_blocks * kDsBlock);
+  const int hi = MASK == MASK_CAUSAL ? min(Skv, q0 + kTileQ) : Skv;
+  const int n_steps = hi > 0 ? (hi + BN - 1) / BN : 0;
+
+  // Gather offsets (bytes within a 4 KB half block) of this lane's chunks:
+  // load k writes LDS rows 16 k + lane / 4; chunk (lane % 4) of a row is
+  // 16 bytes of lane chunk (key, half (lane % 4) / 2), part lane % 2.
+  // A wave whose step lies past Sq reads through an empty resource: zeros.
+  auto issue = [&](int s, char* kb, char* sb) {
+    tile_load<D, BN>(rows_rsrc(K, Skv, s * BN, ROW), kb, wave, lane);
+    const long blk = wave_ok ? ds_block<MASK>(s >> 1, qs, a.n_qs) : 0;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(dsh + (size_t)blk * kDsBlock + (size_t)(s & 1) * (kDsBlock / 2),
+                                               wave_ok ? kDsBlock : 0);  // 4 KB: half of the block
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int j = 16 * k + (lane >> 2), w2 = j >> 5, jl = j & 31;
+      const uint32_t off = (uint32_t)((w2 * 64 + jl + 32 * ((lane & 3) >> 1)) * 32 + 16 * (lane & 1));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(sb + wave * SWAVE + 1024 * k), 16, off, 0, 0, 0);
+    }
+  };
+
+  f32x16 dq[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x16{};
+
+  const int ch = 2 * g16 + ((gi & 3) >> 1);
+  const int half = (gi & 1) * 8;
+  auto step = [&](int s, const char* kb, const char* sb, char* kn, char* sn) {
+    if (s + 1 < n_steps) issue(s + 1, kn, sn);
+    {
+      // K^T rows 32t + 16cc + r00 (+ 8), chunk 4dt + ch: (t ^ 64 dt) + row offset
+      // (as in the other backward kernels); dS^T: the same key rows of the
+      // 64-byte rows of this wave's piece, chunk ch.
+      const int r00 = 4 * hh + (gi >> 2);
+      const int t0 = opaque((row_base<D>(r00) | half) ^ (16 * ch));
+      const int t1 = opaque((row_base<D>(r00 + 8) | half) ^ (16 * ch));
+      const char* sw = sb + opaque(wave * SWAVE + r00 * SROW + ch * 16 + half);
+#pragma unroll
+      for (int kc = 0; kc < BN / 16; ++kc) {
+        const u32x2 slo = lds_read_tr16(sw + 16 * kc * SROW), shi = lds_read_tr16(sw + (16 * kc + 8) * SROW);
+        const u32x4 bfrag = u32x4{slo[0], slo[1], shi[0], shi[1]};
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int rows = 16 * kc * ROW;
+          const u32x2 lo = lds_read_tr16(kb + ((t0 ^ (64 * dt)) + rows));
+          const u32x2 hi2 = lds_read_tr16(kb + ((t1 ^ (64 * dt)) + rows));
+          dq[dt] = mfma_bf16(u32x4{lo[0], lo[1], hi2[0], hi2[1]}, bfrag, dq[dt]);
+        }
+      }
+    }
+    wait_loads();
+    __syncthreads();
+  };
+
+  if (n_steps > 0) {
+    issue(0, sK0, sS0);
+    wait_loads();
+  }
+  __syncthreads();
+  for (int s = 0; s < n_steps; s += 2) {
+    step(s, sK0, sS0, sK1, sS1);
+    if (s + 1 < n_steps) step(s + 1, sK1, sS1, sK0, sS0);
+  }
+
+  // Lane l holds position p = l % 32: query 8 ((p % 16) / 4) + 4 (p / 16) + p % 4.
+  const int qi = qw0 + 8 * ((l32 & 15) >> 2) + 4 * (l32 >> 4) + (l32 & 3);
+  if (qi < Sq) {
+    uint16_t* dQ = (uint16_t*)a.dq + ((size_t)(b * a.Hq + hq) * Sq + qi) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d0 = 32 * dt + 8 * rq + 4 * hh;
+        *(u32x2*)(dQ + d0) = u32x2{pack_bf16(dq[dt][4 * rq] * a.scale, dq[dt][4 * rq + 1] * a.scale),
+                                   pack_bf16(dq[dt][4 * rq + 2] * a.scale, dq[dt][4 * rq + 3] * a.scale)};
+      }
+  }
+}
+
 // ---------------------------------------------------------------- bias gradient
 // grad[h][r] = sum over batches b and query tiles qt of the dQ workgroups'
 // partial rows, entry r - 128 qt of row (b, h, qt), in that fixed order, so
@@ -647,16 +781,36 @@ static hipError_t launch_bwd_mm(const BwdArgs& a, int phases, hipStream_t st) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  // Stored dS (the host sets a.ds only for these variants): the dK/dV kernel
+  // writes dS and the dQ kernel reads it.
+  constexpr bool DS_OK = (MASK == MASK_NONE || MASK == MASK_CAUSAL) && !BM && MOD != MOD_REL_BIAS;
+  const bool use_ds = DS_OK && a.ds != nullptr;
   // dK, dV are written for every key (zero when no query sees it).
   if ((phases & 2) && (long)a.B * a.Hkv * a.n_kt > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK, MOD, BM>), dim3((unsigned)(a.B * a.Hkv * a.n_kt)), dim3(256), 0,
-                       st, a);
+    const dim3 grid((unsigned)(a.B * a.Hkv * a.n_kt));
+    if constexpr (DS_OK) {
+      if (use_ds) {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK, MOD, BM, true>), grid, dim3(256), 0, st, a);
+      } else {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK, MOD, BM>), grid, dim3(256), 0, st, a);
+      }
+    } else {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, MASK, MOD, BM>), grid, dim3(256), 0, st, a);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if ((phases & 4) && rows > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, MASK, MOD, BM>), dim3((unsigned)(a.B * a.Hq * a.n_qt)), dim3(256), 0, st,
-                       a);
+    const dim3 grid((unsigned)(a.B * a.Hq * a.n_qt));
+    if constexpr (DS_OK) {
+      if (use_ds) {
+        hipLaunchKernelGGL((bwd_dq_ds_kernel<D, MASK>), grid, dim3(256), 0, st, a);
+      } else {
+        hipLaunchKernelGGL((bwd_dq_kernel<D, MASK, MOD, BM>), grid, dim3(256), 0, st, a);
+      }
+    } else {
+      hipLaunchKernelGGL((bwd_dq_kernel<D, MASK, MOD, BM>), grid, dim3(256), 0, st, a);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

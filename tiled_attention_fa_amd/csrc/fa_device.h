@@ -180,6 +180,16 @@ __device__ __forceinline__ void bias_chunk_to_lds(const float* table, int len, i
 // Wait until every load this wave issued has landed (vmcnt = 0).
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Wait until every vector memory operation of this wave but the two most
+// recent (vmcnt(2); they complete in issue order) has completed, and every
+// LDS access: the stage loads issued earlier in a step have landed while the
+// step's two trailing stores may still be in flight.
+__device__ __forceinline__ void wait_loads_not_last2() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0072);  // vmcnt 2, expcnt 7 (no wait), lgkmcnt 0
+  asm volatile("" ::: "memory");
+}
+
 // Workgroup barrier without a memory fence: unlike __syncthreads it does not
 // wait for this wave's loads in flight into other LDS buffers.  The empty asm
 // statements keep the compiler from moving memory accesses across it.
