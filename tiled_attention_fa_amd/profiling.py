@@ -1,0 +1,255 @@
+"""rocprofv3 evidence for the benchmark workloads: kernel times, HBM traffic,
+instruction mix and shader clock, summarised into profiles/.
+
+    python -m tiled_attention_fa_amd.profiling run --workload W --out DIR
+        Runs, one rocprofv3 pass per child process (this process never
+        touches the GPU), each under a time limit, from /tmp:
+          kernel trace + stats   bench.py --workload W --steps 10 --warmup 3
+          --pmc FETCH_SIZE       bench.py --workload W --steps 2 --warmup 1
+          --pmc WRITE_SIZE       (same)
+          --pmc SQ_* (8 counters, one pass)
+        and, once per DIR, the same two traffic counters over a plain 1 GiB
+        device copy (bench.py --copy-calibration 1024), which scales the
+        counters' KiB to bytes.
+    python -m tiled_attention_fa_amd.profiling summarize --workload W --out DIR
+        Parses those CSV files and writes profiles/traffic_W.json (read by
+        bench.py for roofline.traffic and the clock) and
+        profiles/W_counters.md (the figures and the commands that made them).
+
+Kernels are grouped by the bench.py timing keys (fwd, bwd_delta, bwd_dkdv,
+bwd_dq, block_mask).  The shader clock under a kernel is SQ_BUSY_CYCLES / 32
+(the counter is summed over the 32 shader engines) over that kernel's
+average duration in the trace pass; the matrix-core busy fraction is
+SQ_VALU_MFMA_BUSY_CYCLES over (kernel cycles x 1024 SIMDs).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+BENCH = os.path.join(ROOT, "bench.py")
+PROFILES = os.path.join(ROOT, "profiles")
+
+SQ_COUNTERS = ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT",
+               "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_SALU"]
+SHADER_ENGINES = 32
+SIMDS = 1024
+COPY_MIB = 1024
+
+
+def kernel_key(name: str) -> str | None:
+    """bench.py's timing key of a library kernel, or None for other kernels."""
+    if "miattn::" not in name:
+        return None
+    for pat, key in (("bwd_delta", "bwd_delta"), ("bwd_dkdv", "bwd_dkdv"), ("bwd_dq", "bwd_dq"),
+                     ("block_mask", "block_mask"), ("fp8_quantize", "fp8_quantize"), ("fwd", "fwd"),
+                     ("bias_grad", "bwd_bias_grad")):
+        if pat in name:
+            return key
+    return None
+
+
+def source_sha() -> str:
+    """Same hash as bench.py: of the kernel sources the counters were taken on."""
+    h = hashlib.sha256()
+    d = os.path.join(HERE, "csrc")
+    for f in sorted(os.listdir(d)):
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _bench_args(workload: str, steps: int, warmup: int, extra=()) -> list[str]:
+    return [sys.executable, BENCH, "--workload", workload, "--no-cpu-baseline", "--steps", str(steps),
+            "--warmup", str(warmup), *extra]
+
+
+def passes(workload: str, out: str) -> list[tuple[str, list[str]]]:
+    """(name, argv) of every rocprofv3 pass of one workload."""
+    wdir = os.path.join(out, workload)
+    fmt = ["--output-format", "csv", "-o", "run"]
+    res = [("trace", ["rocprofv3", "--kernel-trace", "--stats", *fmt, "-d", os.path.join(wdir, "trace"), "--",
+                      *_bench_args(workload, 10, 3)])]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        res.append((c, ["rocprofv3", "--pmc", c, *fmt, "-d", os.path.join(wdir, c), "--",
+                        *_bench_args(workload, 2, 1)]))
+    res.append(("sq", ["rocprofv3", "--pmc", *SQ_COUNTERS, *fmt, "-d", os.path.join(wdir, "sq"), "--",
+                       *_bench_args(workload, 2, 1)]))
+    return res
+
+
+def calibration_passes(out: str) -> list[tuple[str, list[str]]]:
+    fmt = ["--output-format", "csv", "-o", "run"]
+    return [(f"copy_{c}", ["rocprofv3", "--pmc", c, *fmt, "-d", os.path.join(out, f"copy_{c}"), "--",
+                           sys.executable, BENCH, "--copy-calibration", str(COPY_MIB)])
+            for c in ("FETCH_SIZE", "WRITE_SIZE")]
+
+
+def run(workload: str, out: str, limit: int) -> None:
+    out = os.path.abspath(out)
+    os.makedirs(out, exist_ok=True)
+    todo = passes(workload, out)
+    if not os.path.isdir(os.path.join(out, "copy_WRITE_SIZE")):
+        todo = calibration_passes(out) + todo
+    env = dict(os.environ, TMPDIR="/tmp")
+    for name, argv in todo:
+        print(f"profiling: {workload} {name}", flush=True)
+        # The pass's own time limit (a counter request the hardware cannot
+        # serve makes rocprofv3 hang instead of failing).
+        r = subprocess.run(["timeout", "-s", "KILL", str(limit), *argv], cwd="/tmp", env=env,
+                           stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        with open(os.path.join(out, f"{workload}_{name}.log" if not name.startswith("copy") else f"{name}.log"),
+                  "w") as f:
+            f.write(r.stdout)
+        if r.returncode != 0:
+            sys.exit(f"rocprofv3 pass {name} of {workload} ended with status {r.returncode}")
+
+
+def _csv(pattern: str) -> list[dict]:
+    files = sorted(glob.glob(pattern, recursive=True))
+    if not files:
+        raise FileNotFoundError(pattern)
+    rows = []
+    for fn in files:
+        with open(fn, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _dispatch_sums(d: str) -> dict[str, dict[str, float]]:
+    """Per kernel name and counter: mean over dispatches of the per-dispatch sum."""
+    per: dict[tuple[str, str, str], float] = {}
+    for r in _csv(os.path.join(d, "**", "*counter_collection.csv")):
+        key = (r["Kernel_Name"], r["Counter_Name"], r.get("Dispatch_Id") or r.get("Correlation_Id", ""))
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    acc: dict[str, dict[str, list[float]]] = {}
+    for (name, c, _), v in per.items():
+        acc.setdefault(name, {}).setdefault(c, []).append(v)
+    return {n: {c: sum(v) / len(v) for c, v in cs.items()} for n, cs in acc.items()}
+
+
+def trace_stats(d: str) -> dict[str, dict[str, float]]:
+    res = {}
+    for r in _csv(os.path.join(d, "**", "*kernel_stats.csv")):
+        res[r["Name"]] = {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                          "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3,
+                          "total_us": float(r["TotalDurationNs"]) / 1e3}
+    return res
+
+
+def calibration(out: str) -> dict:
+    f = _dispatch_sums(os.path.join(out, "copy_FETCH_SIZE"))
+    w = _dispatch_sums(os.path.join(out, "copy_WRITE_SIZE"))
+    copy = [n for n in f if "copy" in n.lower()]
+    if not copy:
+        raise RuntimeError("no copy kernel in the calibration run")
+    name = max(copy, key=lambda n: f[n].get("FETCH_SIZE", 0.0))
+    nbytes = COPY_MIB << 20
+    fk, wk = f[name]["FETCH_SIZE"], w[name]["WRITE_SIZE"]
+    return {"copy_kernel": name, "copy_bytes": nbytes, "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+            "fetch_factor": nbytes / (fk * 1024.0), "write_factor": nbytes / (wk * 1024.0)}
+
+
+def summarize(workload: str, out: str) -> dict:
+    wdir = os.path.join(out, workload)
+    cal = calibration(out)
+    fetch = _dispatch_sums(os.path.join(wdir, "FETCH_SIZE"))
+    write = _dispatch_sums(os.path.join(wdir, "WRITE_SIZE"))
+    sq = _dispatch_sums(os.path.join(wdir, "sq"))
+    tr = trace_stats(os.path.join(wdir, "trace"))
+    kernels: dict[str, dict] = {}
+    for name, st in sorted(tr.items(), key=lambda kv: -kv[1]["total_us"]):
+        key = kernel_key(name)
+        if key is None:
+            continue
+        k = {"kernel_name": name, "calls": st["calls"], "avg_us": st["avg_us"], "min_us": st["min_us"],
+             "max_us": st["max_us"]}
+        if name in fetch and name in write:
+            fk, wk = fetch[name]["FETCH_SIZE"], write[name]["WRITE_SIZE"]
+            k.update(fetch_kib=fk, write_kib=wk,
+                     bytes_per_launch=int(round(fk * 1024.0 * cal["fetch_factor"] + wk * 1024.0 * cal["write_factor"])))
+        if name in sq:
+            c = sq[name]
+            cycles = c.get("SQ_BUSY_CYCLES", 0.0) / SHADER_ENGINES
+            k["sq"] = c
+            if cycles > 0:
+                k["clock_ghz"] = cycles / (st["avg_us"] * 1e3)
+                k["mfma_busy"] = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (cycles * SIMDS)
+            if c.get("SQ_INSTS_MFMA", 0) > 0:
+                k["valu_per_mfma"] = c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"]
+                k["lds_per_mfma"] = c["SQ_INSTS_LDS"] / c["SQ_INSTS_MFMA"]
+        if key in kernels:  # several kernels under one key (the block-mask builder): the longest
+            if kernels[key]["avg_us"] >= k["avg_us"]:
+                continue
+        kernels[key] = k
+    out_abs = os.path.abspath(out)
+    return {"workload": workload, "source_sha": source_sha(), "calibration": cal, "kernels": kernels,
+            "commands": {n: " ".join("python3" if x == sys.executable else x for x in a)
+                         .replace(out_abs, "<out>").replace(ROOT, "<repo>")
+                         for n, a in passes(workload, out_abs) + calibration_passes(out_abs)}}
+
+
+def write_summary(rec: dict) -> tuple[str, str]:
+    w = rec["workload"]
+    os.makedirs(PROFILES, exist_ok=True)
+    jpath = os.path.join(PROFILES, f"traffic_{w}.json")
+    slim = {"workload": w, "source_sha": rec["source_sha"], "calibration": rec["calibration"],
+            "kernels": {k: {x: v for x, v in d.items() if x != "sq"} for k, d in rec["kernels"].items()}}
+    with open(jpath, "w") as f:
+        json.dump(slim, f, indent=1)
+    lines = [f"# Counters and kernel trace: {w}", "",
+             "Commands (on the GPU host, from /tmp with TMPDIR=/tmp; `<repo>` is the repository root, `<out>` the "
+             "output folder); `python -m tiled_attention_fa_amd.profiling run` issues exactly these:", "", "```"]
+    lines += [rec["commands"][n] for n in ("trace", "FETCH_SIZE", "WRITE_SIZE", "sq", "copy_FETCH_SIZE",
+                                            "copy_WRITE_SIZE")]
+    cal = rec["calibration"]
+    lines += ["```", "",
+              f"Calibration: a {cal['copy_bytes'] >> 20} MiB device copy (`{cal['copy_kernel']}`) reads "
+              f"FETCH_SIZE = {cal['fetch_kib_per_dispatch']:.0f} KiB and WRITE_SIZE = {cal['write_kib_per_dispatch']:.0f}"
+              f" KiB per dispatch: KiB are scaled by {cal['fetch_factor']:.3f} (fetch) and {cal['write_factor']:.3f}"
+              " (write) to bytes.", "",
+              "| key | kernel | calls | avg (us) | min (us) | max (us) | HBM read MB | HBM written MB | clock (GHz) "
+              "| MFMA busy | VALU / MFMA | LDS / MFMA | LDS bank conflicts |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for key, k in rec["kernels"].items():
+        rd = k.get("fetch_kib", 0.0) * 1024 * cal["fetch_factor"] / 1e6
+        wr = k.get("write_kib", 0.0) * 1024 * cal["write_factor"] / 1e6
+        sq = k.get("sq", {})
+
+        def fmt(x, p=2):
+            return "-" if x is None else f"{x:.{p}f}"
+        lines.append(f"| {key} | `{k['kernel_name']}` | {k['calls']} | {k['avg_us']:.1f} | {k['min_us']:.1f} | "
+                     f"{k['max_us']:.1f} | {rd:.1f} | {wr:.1f} | {fmt(k.get('clock_ghz'))} | "
+                     f"{fmt(k.get('mfma_busy'))} | {fmt(k.get('valu_per_mfma'), 1)} | {fmt(k.get('lds_per_mfma'), 2)} | "
+                     f"{sq.get('SQ_LDS_BANK_CONFLICT', 0):.0f} |")
+    lines += ["", f"Kernel sources of these figures: hash `{rec['source_sha']}` (bench.py uses the traffic and clock "
+              "only while the sources hash the same)."]
+    mpath = os.path.join(PROFILES, f"{w}_counters.md")
+    with open(mpath, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return jpath, mpath
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("action", choices=["run", "summarize"])
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--limit", type=int, default=150, help="seconds per rocprofv3 pass")
+    args = ap.parse_args()
+    if args.action == "run":
+        run(args.workload, args.out, args.limit)
+    else:
+        print(*write_summary(summarize(args.workload, args.out)))
+
+
+if __name__ == "__main__":
+    main()
