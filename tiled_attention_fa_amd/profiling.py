@@ -15,6 +15,11 @@ instruction mix and shader clock, summarised into profiles/.
         Parses those CSV files and writes profiles/traffic_W.json (read by
         bench.py for roofline.traffic and the clock) and
         profiles/W_counters.md (the figures and the commands that made them).
+    With --batch B / --seq-len S (both actions) the workload runs at that
+    shape; the summary is then profiles/W_B<B>_S<S>_counters.md, with the
+    compulsory HBM bytes of the shape beside the counters (a shape whose
+    inputs fit the L2 checks the copy calibration on the library's own
+    access pattern), and no traffic file.
 
 Kernels are grouped by the bench.py timing keys (fwd, bwd_delta, bwd_dkdv,
 bwd_dq, block_mask).  The shader clock under a kernel is SQ_BUSY_CYCLES / 32
@@ -67,22 +72,34 @@ def source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def _bench_args(workload: str, steps: int, warmup: int, extra=()) -> list[str]:
+def _bench_args(workload: str, steps: int, warmup: int, shape=(0, 0)) -> list[str]:
+    extra = []
+    if shape[0]:
+        extra += ["--batch", str(shape[0])]
+    if shape[1]:
+        extra += ["--seq-len", str(shape[1])]
     return [sys.executable, BENCH, "--workload", workload, "--no-cpu-baseline", "--steps", str(steps),
             "--warmup", str(warmup), *extra]
 
 
-def passes(workload: str, out: str) -> list[tuple[str, list[str]]]:
+def label(workload: str, shape=(0, 0)) -> str:
+    """Name of a profiled case: the workload, plus its shape when overridden."""
+    if not any(shape):
+        return workload
+    return workload + "".join(f"_{t}{v}" for t, v in zip("BS", shape) if v)
+
+
+def passes(workload: str, out: str, shape=(0, 0)) -> list[tuple[str, list[str]]]:
     """(name, argv) of every rocprofv3 pass of one workload."""
-    wdir = os.path.join(out, workload)
+    wdir = os.path.join(out, label(workload, shape))
     fmt = ["--output-format", "csv", "-o", "run"]
     res = [("trace", ["rocprofv3", "--kernel-trace", "--stats", *fmt, "-d", os.path.join(wdir, "trace"), "--",
-                      *_bench_args(workload, 10, 3)])]
+                      *_bench_args(workload, 10, 3, shape)])]
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         res.append((c, ["rocprofv3", "--pmc", c, *fmt, "-d", os.path.join(wdir, c), "--",
-                        *_bench_args(workload, 2, 1)]))
+                        *_bench_args(workload, 2, 1, shape)]))
     res.append(("sq", ["rocprofv3", "--pmc", *SQ_COUNTERS, *fmt, "-d", os.path.join(wdir, "sq"), "--",
-                       *_bench_args(workload, 2, 1)]))
+                       *_bench_args(workload, 2, 1, shape)]))
     return res
 
 
@@ -93,24 +110,25 @@ def calibration_passes(out: str) -> list[tuple[str, list[str]]]:
             for c in ("FETCH_SIZE", "WRITE_SIZE")]
 
 
-def run(workload: str, out: str, limit: int) -> None:
+def run(workload: str, out: str, limit: int, shape=(0, 0)) -> None:
     out = os.path.abspath(out)
     os.makedirs(out, exist_ok=True)
-    todo = passes(workload, out)
+    todo = passes(workload, out, shape)
+    name_of = label(workload, shape)
     if not os.path.isdir(os.path.join(out, "copy_WRITE_SIZE")):
         todo = calibration_passes(out) + todo
     env = dict(os.environ, TMPDIR="/tmp")
     for name, argv in todo:
-        print(f"profiling: {workload} {name}", flush=True)
+        print(f"profiling: {name_of} {name}", flush=True)
         # The pass's own time limit (a counter request the hardware cannot
         # serve makes rocprofv3 hang instead of failing).
         r = subprocess.run(["timeout", "-s", "KILL", str(limit), *argv], cwd="/tmp", env=env,
                            stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-        with open(os.path.join(out, f"{workload}_{name}.log" if not name.startswith("copy") else f"{name}.log"),
+        with open(os.path.join(out, f"{name_of}_{name}.log" if not name.startswith("copy") else f"{name}.log"),
                   "w") as f:
             f.write(r.stdout)
         if r.returncode != 0:
-            sys.exit(f"rocprofv3 pass {name} of {workload} ended with status {r.returncode}")
+            sys.exit(f"rocprofv3 pass {name} of {name_of} ended with status {r.returncode}")
 
 
 def _csv(pattern: str) -> list[dict]:
@@ -158,8 +176,23 @@ def calibration(out: str) -> dict:
             "fetch_factor": nbytes / (fk * 1024.0), "write_factor": nbytes / (wk * 1024.0)}
 
 
-def summarize(workload: str, out: str) -> dict:
-    wdir = os.path.join(out, workload)
+def compulsory_bytes(workload: str, shape=(0, 0)) -> dict[str, int]:
+    """HBM bytes each forward kernel must move at least, per launch: Q, K, V
+    read once, O and LSE written once (bf16 / fp32 elements as the workload
+    stores them)."""
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import synth  # the workload shapes only
+    w = synth.WORKLOADS[workload]
+    B, S = shape[0] or w.B, shape[1] or w.S
+    el = 4 if w.dtype == "f32" else 2
+    q = B * w.Hq * S * w.D * el
+    kv = 2 * B * w.Hkv * S * w.D * el
+    return {"read": q + kv, "written": q + (B * w.Hq * S * 4 if w.lse else 0)}
+
+
+def summarize(workload: str, out: str, shape=(0, 0)) -> dict:
+    wdir = os.path.join(out, label(workload, shape))
     cal = calibration(out)
     fetch = _dispatch_sums(os.path.join(wdir, "FETCH_SIZE"))
     write = _dispatch_sums(os.path.join(wdir, "WRITE_SIZE"))
@@ -191,21 +224,28 @@ def summarize(workload: str, out: str) -> dict:
                 continue
         kernels[key] = k
     out_abs = os.path.abspath(out)
-    return {"workload": workload, "source_sha": source_sha(), "calibration": cal, "kernels": kernels,
-            "commands": {n: " ".join("python3" if x == sys.executable else x for x in a)
-                         .replace(out_abs, "<out>").replace(ROOT, "<repo>")
-                         for n, a in passes(workload, out_abs) + calibration_passes(out_abs)}}
+    rec = {"workload": workload, "label": label(workload, shape), "source_sha": source_sha(), "calibration": cal,
+           "kernels": kernels,
+           "commands": {n: " ".join("python3" if x == sys.executable else x for x in a)
+                        .replace(out_abs, "<out>").replace(ROOT, "<repo>")
+                        for n, a in passes(workload, out_abs, shape) + calibration_passes(out_abs)}}
+    if any(shape):
+        rec["compulsory"] = compulsory_bytes(workload, shape)
+    return rec
 
 
-def write_summary(rec: dict) -> tuple[str, str]:
+def write_summary(rec: dict) -> tuple[str | None, str]:
     w = rec["workload"]
+    name = rec.get("label", w)
     os.makedirs(PROFILES, exist_ok=True)
-    jpath = os.path.join(PROFILES, f"traffic_{w}.json")
-    slim = {"workload": w, "source_sha": rec["source_sha"], "calibration": rec["calibration"],
-            "kernels": {k: {x: v for x, v in d.items() if x != "sq"} for k, d in rec["kernels"].items()}}
-    with open(jpath, "w") as f:
-        json.dump(slim, f, indent=1)
-    lines = [f"# Counters and kernel trace: {w}", "",
+    jpath = None
+    if name == w:  # bench.py's traffic file belongs to the workload's own shape
+        jpath = os.path.join(PROFILES, f"traffic_{w}.json")
+        slim = {"workload": w, "source_sha": rec["source_sha"], "calibration": rec["calibration"],
+                "kernels": {k: {x: v for x, v in d.items() if x != "sq"} for k, d in rec["kernels"].items()}}
+        with open(jpath, "w") as f:
+            json.dump(slim, f, indent=1)
+    lines = [f"# Counters and kernel trace: {name}", "",
              "Commands (on the GPU host, from /tmp with TMPDIR=/tmp; `<repo>` is the repository root, `<out>` the "
              "output folder); `python -m tiled_attention_fa_amd.profiling run` issues exactly these:", "", "```"]
     lines += [rec["commands"][n] for n in ("trace", "FETCH_SIZE", "WRITE_SIZE", "sq", "copy_FETCH_SIZE",
@@ -230,9 +270,13 @@ def write_summary(rec: dict) -> tuple[str, str]:
                      f"{k['max_us']:.1f} | {rd:.1f} | {wr:.1f} | {fmt(k.get('clock_ghz'))} | "
                      f"{fmt(k.get('mfma_busy'))} | {fmt(k.get('valu_per_mfma'), 1)} | {fmt(k.get('lds_per_mfma'), 2)} | "
                      f"{sq.get('SQ_LDS_BANK_CONFLICT', 0):.0f} |")
+    if "compulsory" in rec:
+        c = rec["compulsory"]
+        lines += ["", f"Compulsory bytes of the forward at this shape (Q, K, V read once; O and LSE written once): "
+                  f"{c['read'] / 1e6:.2f} MB read, {c['written'] / 1e6:.2f} MB written."]
     lines += ["", f"Kernel sources of these figures: hash `{rec['source_sha']}` (bench.py uses the traffic and clock "
               "only while the sources hash the same)."]
-    mpath = os.path.join(PROFILES, f"{w}_counters.md")
+    mpath = os.path.join(PROFILES, f"{name}_counters.md")
     with open(mpath, "w") as f:
         f.write("\n".join(lines) + "\n")
     return jpath, mpath
@@ -244,11 +288,14 @@ def main() -> None:
     ap.add_argument("--workload", required=True)
     ap.add_argument("--out", required=True)
     ap.add_argument("--limit", type=int, default=150, help="seconds per rocprofv3 pass")
+    ap.add_argument("--batch", type=int, default=0, help="run the workload at this batch size")
+    ap.add_argument("--seq-len", type=int, default=0, help="run the workload at this sequence length")
     args = ap.parse_args()
+    shape = (args.batch, args.seq_len)
     if args.action == "run":
-        run(args.workload, args.out, args.limit)
+        run(args.workload, args.out, args.limit, shape)
     else:
-        print(*write_summary(summarize(args.workload, args.out)))
+        print(*[p for p in write_summary(summarize(args.workload, args.out, shape)) if p])
 
 
 if __name__ == "__main__":
