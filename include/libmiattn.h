@@ -147,15 +147,25 @@ typedef struct {
   int32_t* kv_index;         /* [n_b][n_q][n_kv] ascending, first kv_count valid */
   int32_t* q_count;          /* [n_b][n_kv] non-empty q tiles per kv tile */
   int32_t* q_index;          /* [n_b][n_kv][n_q] ascending, first q_count valid */
-  int32_t* q_order;          /* [n_b][n_q] or NULL: the q tiles by descending kv_count
-                                (ties by ascending index).  The query-stationary
-                                kernels start their tiles in this order, longest
-                                first, so the hardware's in-order dispatch to free
-                                compute units balances uneven rows (document
-                                masks).  Rows of more than 2048 tiles get the
-                                identity order.  NULL: the default order. */
-  int32_t* kv_order;         /* [n_b][n_kv] or NULL: the kv tiles by descending
-                                q_count, for the key-stationary dK/dV kernel */
+  int32_t* q_order;          /* [n_b][n_q] or NULL: the q tiles in schedule order,
+                                by descending kv_count, ties by ascending index.
+                                Under a document mask, tiles whose kv lists
+                                start at the same kv tile (one document) stay
+                                together: such groups go by descending weight
+                                (their longest kv_count), ties by ascending
+                                first kv tile, and inside a group by descending
+                                kv_count, ties by ascending index.  The query-
+                                stationary kernels start their tiles in this
+                                order: the longest first, so the hardware's
+                                in-order dispatch to free compute units
+                                balances uneven rows, and one document's tiles
+                                together, so they share its key rows in L2.
+                                Rows of more than 2048 tiles get the identity
+                                order.  NULL: the default order. */
+  int32_t* kv_order;         /* [n_b][n_kv] or NULL: the kv tiles in the same
+                                kind of order (document groups by the last q
+                                tile of their q lists), for the key-stationary
+                                dK/dV kernel */
 } fa_block_mask;
 
 /* Forward pass.  q, k, v, out: device, dtype elements in the layout above.

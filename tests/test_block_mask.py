@@ -47,17 +47,34 @@ def test_builder_matches_brute_force(case):
         for t in range(st.shape[2]):
             n = len(ql[b][t])
             assert qc[b, t] == n and np.array_equal(qi[b, t, :n], ql[b][t]) and np.all(qi[b, t, n:st.shape[1]] == -1)
-    _check_orders(bm, kc, qc)
+    _check_orders(bm, kc, qc, spec["mask"] == 3)
 
 
-def _check_orders(bm, kc, qc):
-    """q_order / kv_order: the tiles by descending list length, ties by index."""
-    for order, cnt in ((bm.q_order, kc), (bm.kv_order, qc)):
+def expected_order(cnt, lists, first, documents=True):
+    """Schedule order of one batch row's tiles: longest list first, ties by
+    index; under a document mask, groups of tiles whose lists share their
+    first (q tiles) or last (kv tiles) entry, heaviest group first (weight:
+    its longest list), ties by ascending group key, and inside a group
+    longest list first, ties by index.  Empty lists form one group keyed
+    past every tile."""
+    n, cap = lists.shape
+    if not documents:
+        return sorted(range(n), key=lambda t: (-int(cnt[t]), t))
+    group = [int(lists[t, 0 if first else cnt[t] - 1]) if cnt[t] > 0 else cap for t in range(n)]
+    weight = {}
+    for t in range(n):
+        weight[group[t]] = max(weight.get(group[t], 0), int(cnt[t]))
+    return sorted(range(n), key=lambda t: (-weight[group[t]], group[t], -int(cnt[t]), t))
+
+
+def _check_orders(bm, kc, qc, documents):
+    """q_order / kv_order against the schedule order above."""
+    ki, qi = bm.kv_index.cpu().numpy(), bm.q_index.cpu().numpy()
+    for order, cnt, lists, first in ((bm.q_order, kc, ki, True), (bm.kv_order, qc, qi, False)):
         o = order.cpu().numpy()
         for b in range(cnt.shape[0]):
             n = cnt.shape[1]
-            want = sorted(range(n), key=lambda t: (-int(cnt[b, t]), t))
-            assert np.array_equal(o[b, :n], want)
+            assert np.array_equal(o[b, :n], expected_order(cnt[b], lists[b], first, documents))
 
 
 def test_doc_config_shape_mask():
@@ -130,7 +147,7 @@ def test_builder_unsorted_doc_ids(pattern):
         for t in range(st.shape[1]):
             n = len(kvl[b][t])
             assert kc[b, t] == n and np.array_equal(ki[b, t, :n], kvl[b][t])
-    _check_orders(bm, kc, bm.q_count.cpu().numpy())
+    _check_orders(bm, kc, bm.q_count.cpu().numpy(), True)
     if pattern == "interleaved":  # the case the id ranges alone cannot decide
         assert (st == 0).sum() > 0 and (st == 1).sum() > 0
 
@@ -138,7 +155,7 @@ def test_builder_unsorted_doc_ids(pattern):
 @pytest.mark.parametrize("mask", [1, 3])
 def test_orders_change_nothing_but_schedule(mask):
     """Forward and backward results are bit-identical with and without the
-    longest-first tile orders (only the workgroup-to-tile map changes)."""
+    schedule orders (only the workgroup-to-tile map changes)."""
     B, H, S, D = 2, 2, 900, 128
     q, k, v = (dev(t) for t in synth.qkv(B, H, H, S, S, D, 77))
     do = dev(synth.randn((B, H, S, D), 78))

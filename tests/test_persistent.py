@@ -30,7 +30,7 @@ CASES = [
     (2, 8, 4, 1300, 1300, 128, "bf16", "causal", False),   # 8 (batch, kv-head) units: one queue per XCD
     (1, 6, 3, 700, 700, 64, "bf16", "none_alibi", False),  # 3 units: a single queue
     (2, 4, 2, 333, 333, 128, "f32", "window", False),
-    (1, 4, 4, 2000, 2000, 128, "bf16", "document", True),  # document mask, longest-first tile order
+    (1, 4, 4, 2000, 2000, 128, "bf16", "document", True),  # document mask, block-mask tile order
     (2, 8, 8, 900, 900, 128, "bf16", "document_alibi", True),
     (1, 16, 16, 1100, 1100, 128, "bf16", "causal_softcap_small", True),
     (1, 4, 2, 500, 333, 64, "bf16", "window_boost", False),

@@ -345,7 +345,7 @@ class BlockMask:
         self.kv_index = view(s.kv_index, n_b * n_q * nkv1, torch.int32, (n_b, n_q, nkv1))
         self.q_count = view(s.q_count, n_b * n_kv, torch.int32, (n_b, n_kv))
         self.q_index = view(s.q_index, n_b * nkv1 * nq1, torch.int32, (n_b, nkv1, nq1))
-        # longest-first tile orders (optional in the C struct)
+        # schedule orders of the tiles (optional in the C struct)
         self.q_order = view(s.q_order, n_b * nq1, torch.int32, (n_b, nq1)) if orders else None
         self.kv_order = view(s.kv_order, n_b * nkv1, torch.int32, (n_b, nkv1)) if orders else None
 
@@ -360,7 +360,8 @@ class BlockMask:
 def build_block_mask(mask: int, B: int, Sq: int, Skv: int, *, window: int = 0, doc_ids=None,
                      device="cuda", stream=None, into: BlockMask | None = None, orders: bool = True) -> BlockMask:
     """Build (or rebuild ``into``, allocating nothing) the block mask of a mask kind;
-    ``orders`` adds the longest-first tile orders the kernels schedule by."""
+    ``orders`` adds the tile orders the kernels schedule by (longest first,
+    the tiles of one document together)."""
     n_b = B if mask == MASK_DOCUMENT else 1
     if doc_ids is not None:
         _dense(doc_ids, "doc_ids", (B, Sq), (_torch().int32,))

@@ -46,8 +46,8 @@ struct BlockMaskArgs {
   int32_t* q_count;
   int32_t* q_index;
   int n_b, n_q, n_kv;
-  int32_t* q_order;   // optional: q tiles, longest kv list first
-  int32_t* kv_order;  // optional: kv tiles, longest q list first
+  int32_t* q_order;   // optional: q tiles in schedule order (longest first, documents together)
+  int32_t* kv_order;  // optional: kv tiles in schedule order
 };
 
 struct FwdArgs {

@@ -16,7 +16,8 @@
 // writes the non-empty tiles in ascending order.
 // Kernel 2: one workgroup per (batch row, key tile), one thread per query
 // tile; a prefix sum writes the ascending list of non-empty query tiles.
-// Kernel 3 (when the caller asks for them): the longest-first tile orders.
+// Kernel 3 (when the caller asks for them): the schedule orders (longest
+// first, tiles of one document together).
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -217,18 +218,28 @@ __global__ __launch_bounds__(256) void block_mask_cols_kernel(BlockMaskArgs m) {
   if (tid == 0) m.q_count[bb * m.n_kv + kt] = count;
 }
 
-// Kernel 3: for each batch row, the q tiles by descending kv_count (grid
-// y = 0) and the kv tiles by descending q_count (y = 1), ties by ascending
-// index: item t goes to position #{u : c[u] > c[t] or (c[u] == c[t] and
-// u < t)}, a permutation, so every position is written exactly once.
+// Kernel 3: for each batch row, the q tiles (grid y = 0) and the kv tiles
+// (y = 1) in a schedule order: longest list first, ties by index.  Under a
+// document mask (`group`), tiles whose lists share their first kv tile (q
+// tiles) or their last q tile (kv tiles), i.e. the tiles of one document,
+// which stream the same key (or query) rows, are kept together: groups go
+// heaviest first (weight: the longest list in the group), ties by ascending
+// group key, and inside a group longest first, ties by index.  Workgroups
+// that run together then share their rows in L2, while the longest work
+// still starts first.  Item t goes to position #{u : key(u) < key(t)} for
+// the strict total order key = (-weight, group, -count, index) (without
+// `group`, every tile is its own group of weight = count): a permutation,
+// so every position is written exactly once.
 // Rows of more tiles than this (sequences over 256K tokens) get the identity
 // order: the quadratic ranking below would cost more than it balances.
 constexpr int kOrderMax = 2048;
 
-__global__ __launch_bounds__(256) void block_mask_order_kernel(BlockMaskArgs m) {
+__global__ __launch_bounds__(256) void block_mask_order_kernel(BlockMaskArgs m, int group) {
   const int bb = blockIdx.x, which = blockIdx.y;
-  const int n = which == 0 ? m.n_q : m.n_kv;
+  const int n = which == 0 ? m.n_q : m.n_kv;      // tiles to order
+  const int len = which == 0 ? m.n_kv : m.n_q;    // list capacity of each tile
   const int32_t* c = which == 0 ? m.kv_count + (size_t)bb * m.n_q : m.q_count + (size_t)bb * m.n_kv;
+  const int32_t* lists = which == 0 ? m.kv_index + (size_t)bb * m.n_q * m.n_kv : m.q_index + (size_t)bb * m.n_kv * m.n_q;
   int32_t* order = which == 0 ? m.q_order : m.kv_order;
   if (order == nullptr) return;
   order += (size_t)bb * n;
@@ -236,16 +247,44 @@ __global__ __launch_bounds__(256) void block_mask_order_kernel(BlockMaskArgs m) 
     for (int t = threadIdx.x; t < n; t += 256) order[t] = t;
     return;
   }
-  __shared__ int sc[kOrderMax];  // the counts, read once
-  for (int t = threadIdx.x; t < n; t += 256) sc[t] = c[t];
+  // Group keys lie in [0, len] (len: empty lists); a document mask has
+  // len == n.  Longer lists (never under a document mask) are not grouped.
+  const bool grouped = group && len <= kOrderMax;
+  __shared__ int sw[kOrderMax + 1];                  // group weights by group key
+  __shared__ unsigned long long skey[kOrderMax];     // the packed sort keys
+  for (int g = threadIdx.x; g <= kOrderMax; g += 256) sw[g] = 0;
+  __syncthreads();
+  // (65535 - weight, group, 65535 - count, index) packs into 16-bit fields
+  // of one 64-bit key (counts clamped to 65535: past 8M keys the order of
+  // such tiles among themselves is by index; the unique index field keeps
+  // the ranking a permutation).
+  int ct_[kOrderMax / 256], gt_[kOrderMax / 256];
+#pragma unroll
+  for (int i = 0; i < kOrderMax / 256; ++i) {
+    const int t = threadIdx.x + 256 * i;
+    if (t < n) {
+      const int ct = min(max(c[t], 0), len);
+      const int gt = !grouped ? t : ct == 0 ? len : min(max(lists[(size_t)t * len + (which == 0 ? 0 : ct - 1)], 0), len);
+      ct_[i] = ct;
+      gt_[i] = gt;
+      if (grouped) atomicMax(&sw[gt], ct);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kOrderMax / 256; ++i) {
+    const int t = threadIdx.x + 256 * i;
+    if (t < n) {
+      const int w = min(grouped ? sw[gt_[i]] : ct_[i], 65535), ct = min(ct_[i], 65535);
+      skey[t] = (unsigned long long)(65535 - w) << 48 | (unsigned long long)gt_[i] << 32 |
+                (unsigned long long)(65535 - ct) << 16 | (unsigned long long)t;
+    }
+  }
   __syncthreads();
   for (int t = threadIdx.x; t < n; t += 256) {
-    const int ct = sc[t];
+    const unsigned long long kt = skey[t];
     int pos = 0;
-    for (int u = 0; u < n; ++u) {
-      const int cu = sc[u];
-      pos += (cu > ct) | ((cu == ct) & (u < t));
-    }
+    for (int u = 0; u < n; ++u) pos += skey[u] < kt;
     order[pos] = t;
   }
 }
@@ -264,7 +303,8 @@ hipError_t launch_block_mask(int mask_kind, int window, const int32_t* doc_ids, 
     if (e != hipSuccess) return e;
   }
   if ((m.q_order != nullptr || m.kv_order != nullptr) && (m.n_q > 0 || m.n_kv > 0)) {
-    hipLaunchKernelGGL(block_mask_order_kernel, dim3((unsigned)m.n_b, 2u), dim3(256), 0, st, m);
+    hipLaunchKernelGGL(block_mask_order_kernel, dim3((unsigned)m.n_b, 2u), dim3(256), 0, st, m,
+                       mask_kind == MASK_DOCUMENT ? 1 : 0);
     return hipGetLastError();
   }
   return hipSuccess;

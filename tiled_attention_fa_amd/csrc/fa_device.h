@@ -366,7 +366,7 @@ __device__ __forceinline__ void row_sum_update(float& l, float& c, float alpha, 
   l = t;
 }
 
-// Tile at position r of a block mask's longest-first order, or `fallback`
+// Tile at position r of a block mask's schedule order, or `fallback`
 // when the mask carries no order.  The entry is clamped into [0, n).
 __device__ __forceinline__ int ordered_tile(const int32_t* order, int n_b, int b, int n, int r, int fallback) {
   if (order == nullptr) return fallback;

@@ -552,7 +552,7 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs& a, int b, int hq, int qt
 
 // Query tile of the static schedule's workgroup P: XCD-pinned (batch, kv
 // head) units, heaviest causal tiles first, or the block mask's
-// longest-first order.
+// schedule order.
 template <int MASK, bool BM>
 __device__ __forceinline__ void fwd_tile_of(const FwdArgs& a, int P, int& b, int& hq, int& qt) {
   decode_work(P, a.B, a.Hq, a.Hkv, a.n_qt, (MASK == MASK_CAUSAL || MASK == MASK_DOCUMENT) && !(BM && a.bm.q_order),
