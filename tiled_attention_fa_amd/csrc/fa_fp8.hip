@@ -31,12 +31,22 @@ typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 
 // FP8 tile rows are D bytes: (256 / D) rows share one 256-byte bank window.
-// The 16-byte chunk c of row r is stored at chunk c ^ f(r), f(r) = (r / (256
-// / D)) mod (D / 16): 16 consecutive rows read at one chunk, and the 8 rows x
-// 2 halves of one chunk that a transposing read gathers, hit distinct banks.
+// The 16-byte chunk c of row r is stored at chunk c ^ f(m), m = r / (256 /
+// D) mod (D / 16).  The K reads (16 lanes of 16 bytes per LDS pass: 16
+// consecutive rows at one chunk) need f one-to-one on every 8 (D = 128) or
+// 4 (D = 64) consecutive m.  The transposing V reads (32 lanes of 8 bytes
+// per pass) take two adjacent chunks c, c ^ 1 of 8 rows; at D = 128 those
+// rows are the pairs m0 + {0, 1, 4, 5} (m0 = 0, 2 mod 8), so f / 2 must
+// also differ over each such set: f swaps the two low bits of m, which
+// keeps f a permutation and meets both.  At D = 64, f = m serves both.
 template <int D>
 __device__ __forceinline__ int swz8(int r, int c) {
-  return c ^ ((r / (256 / D)) & (D / 16 - 1));
+  if constexpr (D == 128) {
+    const int m = (r >> 1) & 7;
+    return c ^ (((m & 1) << 1) | ((m >> 1) & 1) | (m & 4));
+  } else {
+    return c ^ ((r / (256 / D)) & (D / 16 - 1));
+  }
 }
 
 // ROWS rows of an FP8 [rows][D] matrix into an LDS tile in the swz8 layout

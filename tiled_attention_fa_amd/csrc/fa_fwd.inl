@@ -47,7 +47,8 @@ namespace miattn {
 //   relative bias: x = raw scale + T[h][i - j + Skv - 1] (natural units),
 //            mult = log2(e).
 // partial: 0 = no masking (full tile), 1 = the pair is admissible iff j < Skv
-// and j <= qi, 2 = admissible iff ok(j, jr) (jr = c + 4hh).  bias(c):
+// and j <= qi, 3 = iff also qi - j < window, 2 = admissible iff ok(j, jr)
+// (jr = c + 4hh).  bias(c):
 // relative-bias entry of in-step key offset c + 4hh.  qw0: first row of the wave.
 template <int MOD, int NT, typename Ok, typename Bias>
 __device__ __forceinline__ float transform_scores(f32x16 (&st)[NT], int partial, int k0, int qi, int qw0, int hh,
@@ -62,14 +63,35 @@ __device__ __forceinline__ float transform_scores(f32x16 (&st)[NT], int partial,
     plain = R <= 0 || !(k0 + 32 * NT - 1 > qw0 - R && k0 < qw0 + 31 + R);
   }
   // Elementwise mask, one branch per mode for the whole step.
+  // Modes 1 and 3 compare the in-step offset c (a constant per register)
+  // with per-lane bounds taken once per step, relative to k0 + 4hh.
   auto mask_all = [&](float masked) __attribute__((always_inline)) {
+    const int base = k0 + 4 * hh;
     if (partial == 1) {
+      const int hi = min(qi, Skv - 1) - base;
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = k0 + 32 * t + 8 * (r >> 2) + (r & 3) + 4 * hh;
-          st[t][r] = (j < Skv && j <= qi) ? st[t][r] : masked;
+          const int c = 32 * t + 8 * (r >> 2) + (r & 3);
+          st[t][r] = c <= hi ? st[t][r] : masked;
+        }
+    } else if (partial == 3) {
+      // lo <= c <= hi as one unsigned compare; lo is clamped to the step's
+      // first key (no overflow for any window), and a row without keys
+      // here gets an empty range.
+      int lo = max(qi - a.mask.window + 1, base) - base;
+      int span = min(qi, Skv - 1) - base - lo;
+      if (span < 0) {
+        lo = 1 << 30;
+        span = 0;
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 32 * t + 8 * (r >> 2) + (r & 3);
+          st[t][r] = (unsigned)(c - lo) <= (unsigned)span ? st[t][r] : masked;
         }
     } else if (partial == 2) {
 #pragma unroll
@@ -409,6 +431,8 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs& a, int b, int hq, int qt
         }
       } else if constexpr (MASK == MASK_CAUSAL) {
         mode = mode ? 1 : 0;
+      } else if constexpr (MASK == MASK_WINDOW) {
+        mode = mode ? 3 : 0;
       }
       float mult;
       float mb = transform_scores<MOD, NT>(
@@ -744,7 +768,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float* bl = bs + (qi - q0 + 4 - 4 * hh);
     float mult;
     float mb = transform_scores<MOD, NT>(
-        st, cls_s == TILE_PARTIAL ? (MASK == MASK_CAUSAL ? 1 : 2) : 0, k0, qi, qw0, hh, Skv, slope, a,
+        st, cls_s == TILE_PARTIAL ? (MASK == MASK_CAUSAL ? 1 : MASK == MASK_WINDOW ? 3 : 2) : 0, k0, qi, qw0, hh,
+        Skv, slope, a,
         [&](int j, int) { return j < Skv && mask_ok<MASK>(qi, j, window, 0, 0); },
         [&](int c) { return REL ? bl[59 - c] : 0.0f; }, mult);
     mb = half_swap_max(mb);
