@@ -190,3 +190,12 @@ def test_phases_on_two_streams():
     torch.cuda.synchronize()
     for got, want, what in zip(grads, ref, ("dQ", "dK", "dV")):
         assert torch.equal(got, want), what
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S", [(2, 8, 4, 700), (4, 8, 2, 200)])
+def test_xcd_pinned_schedule(B, Hq, Hkv, S):
+    """dQ and dK/dV under the XCD-pinned schedule (B * Hkv a multiple of 8),
+    with GQA groups of 2 and 4 query heads."""
+    got, ref = run_bwd(B, Hq, Hkv, S, 128, dict(mask=1), seed=B * S + 1)
+    for g, r, what in zip(got, ref, ("dQ", "dK", "dV")):
+        check_out(g, r, "bf16", what)

@@ -262,3 +262,14 @@ def test_softcap_mixed_forms(mask):
     o_ref, l_ref = oracle.forward(q, k, v, f32_scale(D), oracle.Variant(**spec))
     check_out(o, o_ref, "bf16")
     check_lse(lse, l_ref)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S", [(2, 8, 4, 700), (1, 16, 8, 1300), (4, 8, 2, 200), (2, 16, 8, 2600)])
+def test_xcd_pinned_schedule(B, Hq, Hkv, S):
+    """B * Hkv a multiple of 8 pins every (batch, kv-head) unit to one XCD,
+    one to four units and one to four query heads per unit on each, at 1 to
+    21 tiles per head (128- and 256-row tiles): every tile of every head must
+    be computed exactly once."""
+    (o, lse), o_ref, l_ref = run_case(B, Hq, Hkv, S, S, 128, "bf16", dict(mask=1), seed=B * S)
+    check_out(o, o_ref, "bf16")
+    check_lse(lse, l_ref)

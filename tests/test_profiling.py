@@ -85,3 +85,35 @@ def test_kernel_keys():
     assert profiling.kernel_key("void miattn::bwd_dq_ds_kernel<128, 1>(miattn::BwdArgs)") == "bwd_dq"
     assert profiling.kernel_key("void miattn::bwd_dkdv_kernel<128, 1, 0, false, false>(miattn::BwdArgs)") == "bwd_dkdv"
     assert profiling.kernel_key(COPY) is None
+
+
+def _fake_bench(label, args):
+    w = args[args.index("--workload") + 1]
+    bwd = w == "causal_fwd_bwd"
+    rec = {"value": 800.0, "ms_per_step": 2.25, "dtype": "bf16", "fwd_tflops": 1000.0, "bwd_tflops": 700.0,
+           "config": {"workload": w, "B": 2, "Hq": 16, "Hkv": 16, "S": 8192, "D": 128, "mask": "causal",
+                      "mod": "none", "window": 0, "pass": "fwd+bwd" if bwd else "fwd", "admissible_pairs": 1000,
+                      "schedule": "persistent" if "persistent" in label else "static",
+                      **({"bwd_dq": "stored" if "stored" in label else "recompute"} if bwd else {})},
+           "kernel_ms": {"fwd": 0.5, **({"bwd_delta": 0.03, "bwd_dkdv": 1.0, "bwd_dq": 0.7} if bwd else {})},
+           "roofline": {"kernel": "bwd_dkdv" if bwd else "fwd", "frac": 0.43}}
+    return "some log line\n" + json.dumps(rec) + "\n"
+
+
+@pytest.mark.parametrize("which,name,rows", [("workloads", "workloads_all_bench.md", 10),
+                                             ("seqlen", "causal_by_seqlen.md", 6),
+                                             ("variants", "schedule_and_dq_variants.md", 24)])
+def test_bench_tables(tmp_path, monkeypatch, which, name, rows):
+    monkeypatch.setattr(profiling, "PROFILES", str(tmp_path / "profiles"))
+    d = tmp_path / "out" / "bench"
+    d.mkdir(parents=True)
+    runs = profiling.bench_runs(which)
+    assert len(runs) == rows and len({lab for lab, _ in runs}) == rows
+    for lab, args in runs:
+        (d / f"{lab}.json").write_text(_fake_bench(lab, args))
+    path = profiling.write_bench_table(which, str(tmp_path / "out"))
+    assert os.path.basename(path) == name
+    table = [ln for ln in open(path).read().splitlines() if ln.startswith("| ") and not ln.startswith("| workload |")
+             and not ln.startswith("| S |") and not ln.startswith("| run |")]
+    assert len(table) == rows
+    assert "python3 bench.py --workload" in open(path).read()

@@ -21,6 +21,16 @@ instruction mix and shader clock, summarised into profiles/.
     inputs fit the L2 checks the copy calibration on the library's own
     access pattern), and no traffic file.
 
+    python -m tiled_attention_fa_amd.profiling bench --set SET --out DIR
+    python -m tiled_attention_fa_amd.profiling bench-summary --set SET --out DIR
+        Plain bench.py runs (no profiler), one child process each under a
+        time limit, their JSON lines kept in DIR/bench/, then one table in
+        profiles/: SET = workloads (every workload at its own shape:
+        workloads_all_bench.md), seqlen (causal fwd+bwd from S = 1024 to
+        32768: causal_by_seqlen.md) or variants (static against persistent
+        schedule, recomputed against stored dS for dQ, each twice, in
+        alternation: schedule_and_dq_variants.md).
+
 Kernels are grouped by the bench.py timing keys (fwd, bwd_delta, bwd_dkdv,
 bwd_dq, block_mask).  The shader clock under a kernel is SQ_BUSY_CYCLES / 32
 (the counter is summed over the 32 shader engines) over that kernel's
@@ -282,16 +292,137 @@ def write_summary(rec: dict) -> tuple[str | None, str]:
     return jpath, mpath
 
 
+# ---------------------------------------------------------------- bench tables
+SEQLEN_SHAPES = [(16, 1024), (8, 2048), (4, 4096), (2, 8192), (1, 16384), (1, 32768)]
+VARIANT_WORKLOADS = ["causal_fwd_bwd", "causal_prefill", "gqa_causal", "gqa_window", "doc_packed"]
+BENCH_STEPS, BENCH_WARMUP = 20, 5
+
+
+def bench_runs(which: str) -> list[tuple[str, list[str]]]:
+    """(label, bench.py arguments) of every run of one table, in run order."""
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import synth  # the workload names only
+    base = ["--no-cpu-baseline", "--steps", str(BENCH_STEPS), "--warmup", str(BENCH_WARMUP)]
+    if which == "workloads":
+        return [(w, ["--workload", w, *base]) for w in synth.WORKLOADS]
+    if which == "seqlen":
+        return [(f"causal_fwd_bwd_B{b}_S{n}", ["--workload", "causal_fwd_bwd", "--batch", str(b), "--seq-len", str(n),
+                                                *base]) for b, n in SEQLEN_SHAPES]
+    if which == "variants":
+        runs = []
+        for rep in (1, 2):
+            for w in VARIANT_WORKLOADS:
+                for sched in ("static", "persistent"):
+                    runs.append((f"{w}_schedule-{sched}_{rep}", ["--workload", w, "--schedule", sched, *base]))
+            for dq in ("recompute", "stored"):
+                runs.append((f"causal_fwd_bwd_dq-{dq}_{rep}", ["--workload", "causal_fwd_bwd", "--bwd-dq", dq, *base]))
+        return runs
+    raise ValueError(which)
+
+
+def run_benches(which: str, out: str, limit: int) -> None:
+    d = os.path.join(os.path.abspath(out), "bench")
+    os.makedirs(d, exist_ok=True)
+    for lab, args in bench_runs(which):
+        print(f"bench: {lab}", flush=True)
+        r = subprocess.run(["timeout", "-s", "KILL", str(limit), sys.executable, BENCH, *args], cwd=ROOT,
+                           stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        with open(os.path.join(d, f"{lab}.json"), "w") as f:
+            f.write(r.stdout)
+        if r.returncode != 0:
+            sys.exit(f"bench.py {' '.join(args)} ended with status {r.returncode}")
+
+
+def _bench_line(path: str) -> dict:
+    for line in reversed(open(path).read().splitlines()):
+        if line.startswith("{"):
+            return json.loads(line)
+    raise ValueError(f"no JSON line in {path}")
+
+
+def _kernel_ms(rec: dict) -> str:
+    return ", ".join(f"{k} {v:.3f}" for k, v in rec.get("kernel_ms", {}).items())
+
+
+def write_bench_table(which: str, out: str) -> str:
+    d = os.path.join(out, "bench")
+    runs = bench_runs(which)
+    recs = [(lab, args, _bench_line(os.path.join(d, f"{lab}.json"))) for lab, args in runs]
+    cmd = "python3 bench.py " + " ".join(runs[0][1])
+    lines = []
+    if which == "workloads":
+        lines += ["# All workloads, one MI355X", "",
+                  "Command (repository root on the GPU host), one run per workload (the first shown; "
+                  "`python -m tiled_attention_fa_amd.profiling bench --set workloads` runs them all):", "",
+                  "```", cmd, "```", "",
+                  "Timed region: the listed kernels per step with inputs resident in HBM (`block_mask` is the mask "
+                  "builder, counted in the step for the document workload). TFLOP/s = 4·D per admissible pair "
+                  "(forward) + 10·D (backward), over Hq.", "",
+                  "| workload | shape | mask | mod | pass | dtype | admissible pairs | ms / step | TFLOP/s | kernel ms "
+                  "| dominant kernel | its frac of 2516.6 |",
+                  "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+        for lab, _, r in recs:
+            c = r["config"]
+            mask = c["mask"] + (f" w={c['window']}" if c.get("window") else "")
+            lines.append(f"| {lab} | B{c['B']} Hq{c['Hq']} Hkv{c['Hkv']} S{c['S']} D{c['D']} | {mask} | {c['mod']} | "
+                         f"{c['pass']} | {r['dtype']} | {c['admissible_pairs']:,} | {r['ms_per_step']:.4f} | "
+                         f"{r['value']:.1f} | {_kernel_ms(r)} | {r['roofline']['kernel']} | "
+                         f"{r['roofline']['frac']:.3f} |")
+        name = "workloads_all_bench.md"
+    elif which == "seqlen":
+        lines += ["# Causal forward + backward by sequence length, H=16, D=128, bf16, one MI355X", "",
+                  "Command (repository root on the GPU host), B x S = 16384 tokens up to S = 16384, then B = 1 "
+                  "(the first shown):", "", "```", cmd, "```", "",
+                  "TFLOP/s count admissible pairs only (4 D forward, 10 D backward). Kernel times are HIP-event "
+                  f"averages over {BENCH_STEPS} steps after {BENCH_WARMUP} warm-up steps.", "",
+                  "| S | B | fwd+bwd TFLOP/s | fwd TFLOP/s | bwd TFLOP/s | fwd ms | delta ms | dK/dV ms | dQ ms |",
+                  "|---|---|---|---|---|---|---|---|---|"]
+        for lab, _, r in recs:
+            c, k = r["config"], r["kernel_ms"]
+            lines.append(f"| {c['S']} | {c['B']} | {r['value']:.1f} | {r['fwd_tflops']:.1f} | {r['bwd_tflops']:.1f} | "
+                         f"{k['fwd']:.3f} | {k['bwd_delta']:.3f} | {k['bwd_dkdv']:.3f} | {k['bwd_dq']:.3f} |")
+        name = "causal_by_seqlen.md"
+    else:
+        lines += ["# Schedule and dQ variants, one MI355X", "",
+                  "Each workload with the static schedule (default) and the persistent work-queue schedule "
+                  "(`--schedule persistent`), and the causal fwd+bwd with dQ recomputed (default) or read from the "
+                  "dS blocks the dK/dV kernel stores (`--bwd-dq stored`); two rounds of all runs in alternation on "
+                  "one box. Command of the first run:", "", "```", cmd, "```", "",
+                  "| run | workload | schedule | dQ | ms / step | TFLOP/s | kernel ms |", "|---|---|---|---|---|---|---|"]
+        for lab, _, r in recs:
+            c = r["config"]
+            lines.append(f"| {lab} | {c['workload']} | {c['schedule']} | {c.get('bwd_dq', '-')} | "
+                         f"{r['ms_per_step']:.4f} | {r['value']:.1f} | {_kernel_ms(r)} |")
+        name = "schedule_and_dq_variants.md"
+    path = os.path.join(PROFILES, name)
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("action", choices=["run", "summarize"])
-    ap.add_argument("--workload", required=True)
+    ap.add_argument("action", choices=["run", "summarize", "bench", "bench-summary"])
+    ap.add_argument("--workload")
+    ap.add_argument("--set", choices=["workloads", "seqlen", "variants"])
     ap.add_argument("--out", required=True)
     ap.add_argument("--limit", type=int, default=150, help="seconds per rocprofv3 pass")
     ap.add_argument("--batch", type=int, default=0, help="run the workload at this batch size")
     ap.add_argument("--seq-len", type=int, default=0, help="run the workload at this sequence length")
     args = ap.parse_args()
     shape = (args.batch, args.seq_len)
+    if args.action in ("bench", "bench-summary"):
+        if not args.set:
+            ap.error("--set is required")
+        if args.action == "bench":
+            run_benches(args.set, args.out, max(args.limit, 300))
+        else:
+            print(write_bench_table(args.set, args.out))
+        return
+    if not args.workload:
+        ap.error("--workload is required")
     if args.action == "run":
         run(args.workload, args.out, args.limit, shape)
     else:
