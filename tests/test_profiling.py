@@ -11,23 +11,31 @@ FWD = "void miattn::fwd_pp_kernel<128, 1, 0>(miattn::FwdArgs)"
 COPY = "__amd_rocclr_copyBuffer"
 
 
-def _counters(path, rows):
+def _counters(path, rows, dur_ns=None):
+    """rows: (dispatch, kernel, counter, value); dur_ns: dispatch -> duration."""
     os.makedirs(path, exist_ok=True)
     with open(os.path.join(path, "run_counter_collection.csv"), "w", newline="") as f:
-        w = csv.DictWriter(f, ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w = csv.DictWriter(f, ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp",
+                               "End_Timestamp"])
         w.writeheader()
         for d, k, c, v in rows:
-            w.writerow({"Dispatch_Id": d, "Kernel_Name": k, "Counter_Name": c, "Counter_Value": v})
+            t0 = 1000 * d
+            w.writerow({"Dispatch_Id": d, "Kernel_Name": k, "Counter_Name": c, "Counter_Value": v,
+                        "Start_Timestamp": t0, "End_Timestamp": t0 + (dur_ns or {}).get(d, 1)})
 
 
-def _stats(path, rows):
+def _trace(path, rows):
+    """rows: (kernel, [durations in ns, in dispatch order])."""
     os.makedirs(path, exist_ok=True)
-    with open(os.path.join(path, "run_kernel_stats.csv"), "w", newline="") as f:
-        w = csv.DictWriter(f, ["Name", "Calls", "TotalDurationNs", "AverageNs", "MinNs", "MaxNs"])
+    with open(os.path.join(path, "run_kernel_trace.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
         w.writeheader()
-        for name, calls, avg in rows:
-            w.writerow({"Name": name, "Calls": calls, "TotalDurationNs": calls * avg, "AverageNs": avg,
-                        "MinNs": avg, "MaxNs": avg})
+        d = 0
+        for name, durs in rows:
+            for t in durs:
+                d += 1
+                w.writerow({"Dispatch_Id": d, "Kernel_Name": name, "Start_Timestamp": 10**9 * d,
+                            "End_Timestamp": 10**9 * d + t})
 
 
 @pytest.fixture
@@ -38,14 +46,23 @@ def fake_run(tmp_path, monkeypatch):
     _counters(out / "copy_FETCH_SIZE", [(1, COPY, "FETCH_SIZE", mib / 2048)])
     _counters(out / "copy_WRITE_SIZE", [(1, COPY, "WRITE_SIZE", mib / 1024)])
     w = out / "gqa_causal_B1_S2048"
-    # Two dispatches; each dispatch's counter is split over two rows (summed).
-    _counters(w / "FETCH_SIZE", [(1, FWD, "FETCH_SIZE", 3000), (1, FWD, "FETCH_SIZE", 1000),
-                                 (2, FWD, "FETCH_SIZE", 2500), (2, FWD, "FETCH_SIZE", 1500)])
-    _counters(w / "WRITE_SIZE", [(1, FWD, "WRITE_SIZE", 500), (2, FWD, "WRITE_SIZE", 700)])
+    n = profiling.BENCH_WARMUP + profiling.BENCH_STEPS
+    # Every dispatch's counter is split over two rows (summed); the warm-up
+    # dispatches read differently and must be left out.
+    fetch, write = [], []
+    for d in range(1, n + 1):
+        warm = d <= profiling.BENCH_WARMUP
+        fetch += [(d, FWD, "FETCH_SIZE", 9000 if warm else 3000), (d, FWD, "FETCH_SIZE", 1000)]
+        write += [(d, FWD, "WRITE_SIZE", 9000 if warm else 600)]
+    _counters(w / "FETCH_SIZE", fetch)
+    _counters(w / "WRITE_SIZE", write)
     sq = {"SQ_BUSY_CYCLES": 32 * 1.5e5, "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * 1.5e5 * 1024, "SQ_INSTS_VALU": 730,
           "SQ_INSTS_MFMA": 100, "SQ_INSTS_LDS": 150, "SQ_LDS_BANK_CONFLICT": 0}
-    _counters(w / "sq", [(1, FWD, c, v) for c, v in sq.items()])
-    _stats(w / "trace", [(FWD, 13, 100e3), ("some_torch_kernel", 5, 1e3)])
+    # 1.5e5 cycles in 100 us (1.5 GHz) per timed dispatch; warm-up dispatches take 300 us.
+    _counters(w / "sq", [(d, FWD, c, v) for d in range(1, n + 1) for c, v in sq.items()],
+              {d: 300e3 if d <= profiling.BENCH_WARMUP else 100e3 for d in range(1, n + 1)})
+    _trace(w / "trace", [(FWD, [400e3] * profiling.BENCH_WARMUP + [100e3, 110e3, 90e3] + [100e3] *
+                          (profiling.BENCH_STEPS - 3)), ("some_torch_kernel", [1e3] * 5)])
     monkeypatch.setattr(profiling, "PROFILES", str(tmp_path / "profiles"))
     return out
 
@@ -59,6 +76,9 @@ def test_summary_scales_and_derives(fake_run, tmp_path):
     assert k["fetch_kib"] == pytest.approx(4000) and k["write_kib"] == pytest.approx(600)
     assert k["bytes_per_launch"] == round(4000 * 1024 * 2 + 600 * 1024)
     assert k["clock_ghz"] == pytest.approx(1.5)  # 1.5e5 cycles in 100 us
+    assert k["timed_calls"] == profiling.BENCH_STEPS and k["calls"] == profiling.BENCH_STEPS + profiling.BENCH_WARMUP
+    assert k["avg_us"] == pytest.approx(100.0) and k["min_us"] == pytest.approx(90.0)
+    assert k["max_us"] == pytest.approx(110.0) and k["avg_all_us"] > 150.0
     assert k["mfma_busy"] == pytest.approx(0.5)
     assert k["valu_per_mfma"] == pytest.approx(7.3) and k["lds_per_mfma"] == pytest.approx(1.5)
     # Compulsory forward bytes of B1 Hq32 Hkv8 S2048 D128 bf16.

@@ -3,10 +3,11 @@ instruction mix and shader clock, summarised into profiles/.
 
     python -m tiled_attention_fa_amd.profiling run --workload W --out DIR
         Runs, one rocprofv3 pass per child process (this process never
-        touches the GPU), each under a time limit, from /tmp:
-          kernel trace + stats   bench.py --workload W --steps 10 --warmup 3
-          --pmc FETCH_SIZE       bench.py --workload W --steps 2 --warmup 1
-          --pmc WRITE_SIZE       (same)
+        touches the GPU), each under a time limit, from /tmp, every pass
+        over bench.py --workload W --steps 20 --warmup 5 (its defaults):
+          kernel trace + stats
+          --pmc FETCH_SIZE
+          --pmc WRITE_SIZE
           --pmc SQ_* (8 counters, one pass)
         and, once per DIR, the same two traffic counters over a plain 1 GiB
         device copy (bench.py --copy-calibration 1024), which scales the
@@ -32,10 +33,12 @@ instruction mix and shader clock, summarised into profiles/.
         alternation: schedule_and_dq_variants.md).
 
 Kernels are grouped by the bench.py timing keys (fwd, bwd_delta, bwd_dkdv,
-bwd_dq, block_mask).  The shader clock under a kernel is SQ_BUSY_CYCLES / 32
-(the counter is summed over the 32 shader engines) over that kernel's
-average duration in the trace pass; the matrix-core busy fraction is
-SQ_VALU_MFMA_BUSY_CYCLES over (kernel cycles x 1024 SIMDs).
+bwd_dq, block_mask).  Durations and counters are taken over the dispatches
+of bench.py's timed steps (a kernel launched once per step: its last 20).
+The shader clock under a kernel is SQ_BUSY_CYCLES / 32 (the counter is
+summed over the 32 shader engines) over each dispatch's own duration in the
+SQ run, averaged; the matrix-core busy fraction is SQ_VALU_MFMA_BUSY_CYCLES
+over (kernel cycles x 1024 SIMDs).
 """
 from __future__ import annotations
 
@@ -58,6 +61,8 @@ SQ_COUNTERS = ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ
 SHADER_ENGINES = 32
 SIMDS = 1024
 COPY_MIB = 1024
+# Every profiled run and every bench-table run: bench.py's default step counts.
+BENCH_STEPS, BENCH_WARMUP = 20, 5
 
 
 def kernel_key(name: str) -> str | None:
@@ -100,16 +105,15 @@ def label(workload: str, shape=(0, 0)) -> str:
 
 
 def passes(workload: str, out: str, shape=(0, 0)) -> list[tuple[str, list[str]]]:
-    """(name, argv) of every rocprofv3 pass of one workload."""
+    """(name, argv) of every rocprofv3 pass of one workload: each runs
+    bench.py's default step counts, so the timed dispatches are bench.py's."""
     wdir = os.path.join(out, label(workload, shape))
     fmt = ["--output-format", "csv", "-o", "run"]
-    res = [("trace", ["rocprofv3", "--kernel-trace", "--stats", *fmt, "-d", os.path.join(wdir, "trace"), "--",
-                      *_bench_args(workload, 10, 3, shape)])]
+    args = _bench_args(workload, BENCH_STEPS, BENCH_WARMUP, shape)
+    res = [("trace", ["rocprofv3", "--kernel-trace", "--stats", *fmt, "-d", os.path.join(wdir, "trace"), "--", *args])]
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
-        res.append((c, ["rocprofv3", "--pmc", c, *fmt, "-d", os.path.join(wdir, c), "--",
-                        *_bench_args(workload, 2, 1, shape)]))
-    res.append(("sq", ["rocprofv3", "--pmc", *SQ_COUNTERS, *fmt, "-d", os.path.join(wdir, "sq"), "--",
-                       *_bench_args(workload, 2, 1, shape)]))
+        res.append((c, ["rocprofv3", "--pmc", c, *fmt, "-d", os.path.join(wdir, c), "--", *args]))
+    res.append(("sq", ["rocprofv3", "--pmc", *SQ_COUNTERS, *fmt, "-d", os.path.join(wdir, "sq"), "--", *args]))
     return res
 
 
@@ -152,24 +156,53 @@ def _csv(pattern: str) -> list[dict]:
     return rows
 
 
-def _dispatch_sums(d: str) -> dict[str, dict[str, float]]:
-    """Per kernel name and counter: mean over dispatches of the per-dispatch sum."""
-    per: dict[tuple[str, str, str], float] = {}
+def _timed(seq: list) -> list:
+    """The dispatches of bench.py's timed steps: a kernel launched once per
+    step has BENCH_WARMUP + BENCH_STEPS dispatches and keeps the last
+    BENCH_STEPS; kernels launched outside the step loop keep all."""
+    return seq[-BENCH_STEPS:] if len(seq) >= BENCH_STEPS + BENCH_WARMUP else seq
+
+
+def _dispatches(d: str) -> dict[str, list[dict[str, float]]]:
+    """Per kernel name, in dispatch order: each dispatch's counters (summed
+    over the rows rocprofv3 splits them into) and its duration in ns."""
+    per: dict[str, dict[int, dict[str, float]]] = {}
     for r in _csv(os.path.join(d, "**", "*counter_collection.csv")):
-        key = (r["Kernel_Name"], r["Counter_Name"], r.get("Dispatch_Id") or r.get("Correlation_Id", ""))
-        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
-    acc: dict[str, dict[str, list[float]]] = {}
-    for (name, c, _), v in per.items():
-        acc.setdefault(name, {}).setdefault(c, []).append(v)
-    return {n: {c: sum(v) / len(v) for c, v in cs.items()} for n, cs in acc.items()}
+        disp = per.setdefault(r["Kernel_Name"], {}).setdefault(int(r.get("Dispatch_Id") or r["Correlation_Id"]), {})
+        c = r["Counter_Name"]
+        disp[c] = disp.get(c, 0.0) + float(r["Counter_Value"])
+        if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+            disp["_dur_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    return {n: [ds[i] for i in sorted(ds)] for n, ds in per.items()}
+
+
+def _dispatch_sums(d: str) -> dict[str, dict[str, float]]:
+    """Per kernel name and counter: mean over the timed dispatches."""
+    res = {}
+    for name, seq in _dispatches(d).items():
+        seq = _timed(seq)
+        keys = {c for x in seq for c in x if not c.startswith("_")}
+        res[name] = {c: sum(x.get(c, 0.0) for x in seq) / len(seq) for c in keys}
+        clocks = [x["SQ_BUSY_CYCLES"] / SHADER_ENGINES / x["_dur_ns"] for x in seq
+                  if x.get("_dur_ns", 0) > 0 and "SQ_BUSY_CYCLES" in x]
+        if clocks:
+            res[name]["_clock_ghz"] = sum(clocks) / len(clocks)
+    return res
 
 
 def trace_stats(d: str) -> dict[str, dict[str, float]]:
+    """Per kernel name: durations of the timed dispatches (average, min,
+    max, in us) and the average over every dispatch."""
+    per: dict[str, list[tuple[int, float]]] = {}
+    for r in _csv(os.path.join(d, "**", "*kernel_trace.csv")):
+        per.setdefault(r["Kernel_Name"], []).append(
+            (int(r["Dispatch_Id"]), (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) / 1e3))
     res = {}
-    for r in _csv(os.path.join(d, "**", "*kernel_stats.csv")):
-        res[r["Name"]] = {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
-                          "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3,
-                          "total_us": float(r["TotalDurationNs"]) / 1e3}
+    for name, v in per.items():
+        allv = [t for _, t in sorted(v)]
+        tv = _timed(allv)
+        res[name] = {"calls": len(allv), "timed_calls": len(tv), "avg_us": sum(tv) / len(tv), "min_us": min(tv),
+                     "max_us": max(tv), "avg_all_us": sum(allv) / len(allv), "total_us": sum(allv)}
     return res
 
 
@@ -213,18 +246,20 @@ def summarize(workload: str, out: str, shape=(0, 0)) -> dict:
         key = kernel_key(name)
         if key is None:
             continue
-        k = {"kernel_name": name, "calls": st["calls"], "avg_us": st["avg_us"], "min_us": st["min_us"],
-             "max_us": st["max_us"]}
+        k = {"kernel_name": name, "calls": st["calls"], "timed_calls": st["timed_calls"], "avg_us": st["avg_us"],
+             "min_us": st["min_us"], "max_us": st["max_us"], "avg_all_us": st["avg_all_us"]}
         if name in fetch and name in write:
             fk, wk = fetch[name]["FETCH_SIZE"], write[name]["WRITE_SIZE"]
             k.update(fetch_kib=fk, write_kib=wk,
                      bytes_per_launch=int(round(fk * 1024.0 * cal["fetch_factor"] + wk * 1024.0 * cal["write_factor"])))
         if name in sq:
-            c = sq[name]
+            c = {x: v for x, v in sq[name].items() if not x.startswith("_")}
             cycles = c.get("SQ_BUSY_CYCLES", 0.0) / SHADER_ENGINES
             k["sq"] = c
             if cycles > 0:
-                k["clock_ghz"] = cycles / (st["avg_us"] * 1e3)
+                # The clock of the counter run's own dispatches (their cycles
+                # over their durations); the trace run's average otherwise.
+                k["clock_ghz"] = sq[name].get("_clock_ghz", cycles / (st["avg_us"] * 1e3))
                 k["mfma_busy"] = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (cycles * SIMDS)
             if c.get("SQ_INSTS_MFMA", 0) > 0:
                 k["valu_per_mfma"] = c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"]
@@ -266,9 +301,13 @@ def write_summary(rec: dict) -> tuple[str | None, str]:
               f"FETCH_SIZE = {cal['fetch_kib_per_dispatch']:.0f} KiB and WRITE_SIZE = {cal['write_kib_per_dispatch']:.0f}"
               f" KiB per dispatch: KiB are scaled by {cal['fetch_factor']:.3f} (fetch) and {cal['write_factor']:.3f}"
               " (write) to bytes.", "",
-              "| key | kernel | calls | avg (us) | min (us) | max (us) | HBM read MB | HBM written MB | clock (GHz) "
-              "| MFMA busy | VALU / MFMA | LDS / MFMA | LDS bank conflicts |",
-              "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+              f"Durations: the kernel trace's timed dispatches (a kernel launched once per step: the last "
+              f"{BENCH_STEPS} of {BENCH_WARMUP} + {BENCH_STEPS}, the dispatches bench.py times; others: all), with the "
+              "average over every dispatch beside them. Counters: the mean over the same dispatches of each counter "
+              "run; the clock is each dispatch's SQ_BUSY_CYCLES / 32 over its own duration in the SQ run.", "",
+              "| key | kernel | timed / all calls | avg (us) | min (us) | max (us) | avg all (us) | HBM read MB "
+              "| HBM written MB | clock (GHz) | MFMA busy | VALU / MFMA | LDS / MFMA | LDS bank conflicts |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for key, k in rec["kernels"].items():
         rd = k.get("fetch_kib", 0.0) * 1024 * cal["fetch_factor"] / 1e6
         wr = k.get("write_kib", 0.0) * 1024 * cal["write_factor"] / 1e6
@@ -276,8 +315,9 @@ def write_summary(rec: dict) -> tuple[str | None, str]:
 
         def fmt(x, p=2):
             return "-" if x is None else f"{x:.{p}f}"
-        lines.append(f"| {key} | `{k['kernel_name']}` | {k['calls']} | {k['avg_us']:.1f} | {k['min_us']:.1f} | "
-                     f"{k['max_us']:.1f} | {rd:.1f} | {wr:.1f} | {fmt(k.get('clock_ghz'))} | "
+        lines.append(f"| {key} | `{k['kernel_name']}` | {k.get('timed_calls', k['calls'])} / {k['calls']} | "
+                     f"{k['avg_us']:.1f} | {k['min_us']:.1f} | {k['max_us']:.1f} | {k.get('avg_all_us', k['avg_us']):.1f} | "
+                     f"{rd:.1f} | {wr:.1f} | {fmt(k.get('clock_ghz'))} | "
                      f"{fmt(k.get('mfma_busy'))} | {fmt(k.get('valu_per_mfma'), 1)} | {fmt(k.get('lds_per_mfma'), 2)} | "
                      f"{sq.get('SQ_LDS_BANK_CONFLICT', 0):.0f} |")
     if "compulsory" in rec:
@@ -295,7 +335,6 @@ def write_summary(rec: dict) -> tuple[str | None, str]:
 # ---------------------------------------------------------------- bench tables
 SEQLEN_SHAPES = [(16, 1024), (8, 2048), (4, 4096), (2, 8192), (1, 16384), (1, 32768)]
 VARIANT_WORKLOADS = ["causal_fwd_bwd", "causal_prefill", "gqa_causal", "gqa_window", "doc_packed"]
-BENCH_STEPS, BENCH_WARMUP = 20, 5
 
 
 def bench_runs(which: str) -> list[tuple[str, list[str]]]:
