@@ -252,6 +252,9 @@ def main():
     ap.add_argument("--schedule", choices=["static", "persistent"], default="static",
                     help="persistent: the forward takes its query tiles from a work queue "
                          "(fa_mask_params.work_queue)")
+    ap.add_argument("--wg-trace", default="", metavar="FILE.npy",
+                    help="after the timed steps, run one more step whose forward records each query tile's "
+                         "start, end, compute unit and size (fa_mask_params.wg_trace) and save the records")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times) and exit: the reference for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -334,7 +337,8 @@ def main():
             i += 1
             if evs:
                 evs[i].record(stream)
-        fa.forward(q, k, v, out=out, lse=lse, return_lse=w.lse or w.backward, block_mask=bm, work_queue=wq, **kw)
+        fa.forward(q, k, v, out=out, lse=lse, return_lse=w.lse or w.backward, block_mask=bm, work_queue=wq,
+                   wg_trace=trace_buf[0], **kw)
         i += 1
         if evs:
             evs[i].record(stream)
@@ -345,6 +349,7 @@ def main():
                 if evs:
                     evs[i].record(stream)
 
+    trace_buf = [None]  # set for the one traced step after the timed ones (--wg-trace)
     for _ in range(args.warmup):
         step(None)
     torch.cuda.synchronize()
@@ -359,6 +364,17 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(end) / args.steps
+    if args.wg_trace:
+        # One more step, untimed, its forward recording where and when each
+        # query tile ran (fa_mask_params.wg_trace; static schedule only).
+        if is_fp8 or wq is not None:
+            sys.exit("--wg-trace covers the bf16/fp32 forward with the static schedule")
+        import numpy as np
+        trace_buf[0] = fa.new_wg_trace(w.B, w.Hq, w.S, dev)
+        step(None)
+        torch.cuda.synchronize()
+        np.save(args.wg_trace, trace_buf[0].cpu().numpy())
+        trace_buf[0] = None
     per_step = {n: sorted(e[i].elapsed_time(e[i + 1]) for e in evs) for i, n in enumerate(names)}
     kernel_ms = {n: sum(t) / args.steps for n, t in per_step.items()}
 
@@ -401,6 +417,7 @@ def main():
         "kernel_ms_median": {n: round(statistics.median(t), 4) for n, t in per_step.items()},
         "kernel_ms_min": {n: round(t[0], 4) for n, t in per_step.items()},
         "wall_s": round(wall, 3),
+        **({"wg_trace": args.wg_trace} if args.wg_trace else {}),
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": None if reshaped else measured_traffic(w.name, dominant)},

@@ -104,7 +104,26 @@ typedef struct {
                               time need separate arrays.  Results are
                               bit-identical to the static schedule's.  NULL:
                               the static schedule.  Ignored by fa_bwd. */
+  int64_t* wg_trace;       /* optional debug output, device int64
+                              [B * Hq * ceil(Sq/128)][FA_WG_TRACE_WORDS]:
+                              fa_fwd writes one record per query tile it
+                              processes, at the tile's index P in the static
+                              schedule (0 <= P < the number of tiles, which is
+                              B * Hq * ceil(Sq/256) for the 256-row kernel
+                              that bf16 forwards of more than 1024 keys with
+                              analytic masks take; records past it are left
+                              untouched): [0] the GPU's constant 100 MHz
+                              clock (s_memrealtime) when the tile starts,
+                              [1] the same after its last output is issued,
+                              [2] the XCC_ID hardware register << 32 | the
+                              HW_ID register of the workgroup's first wave,
+                              [3] the tile's query rows << 32 | its key
+                              steps.  Static schedule only: ignored with a
+                              work_queue, and by fa_bwd.  NULL in production. */
 } fa_mask_params;
+
+/* Words per record of fa_mask_params.wg_trace. */
+#define FA_WG_TRACE_WORDS 4
 
 /* Length of fa_mask_params.work_queue. */
 #define FA_WORK_QUEUE_INTS 288

@@ -87,6 +87,41 @@ def test_fwd_rejects_misaligned_work_queue():
     assert fwd(mp=fa.FaMaskParams(0, None, None, 0x100002)) == fa.FA_ERR_ALIGN
 
 
+def test_fwd_rejects_misaligned_wg_trace():
+    assert fwd(mp=fa.FaMaskParams(0, None, None, None, 0x100004)) == fa.FA_ERR_ALIGN
+
+
+def test_header_constants_match_binding():
+    defines = dict(re.findall(r"^#define\s+(FA_\w+)\s+(.+)$", open(HEADER).read(), flags=re.M))
+    assert int(defines["FA_WORK_QUEUE_INTS"]) == fa.FA_WORK_QUEUE_INTS
+    assert int(defines["FA_WG_TRACE_WORDS"]) == fa.FA_WG_TRACE_WORDS
+    assert eval(defines["FA_NOALLOC_SCRATCH_BYTES"].replace("(size_t)", "")) == fa.FA_NOALLOC_SCRATCH_BYTES
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """sizeof and every field offset of the parameter structs, from a C
+    program compiled against the header, equal the ctypes binding's."""
+    structs = {"fa_mask_params": fa.FaMaskParams, "fa_mod_params": fa.FaModParams,
+               "fa_block_mask": fa.FaBlockMask}
+    src = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"', "int main(void) {"]
+    for cname, cls in structs.items():
+        src.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in cls._fields_:
+            src.append(f'printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    src += ["return 0;", "}"]
+    (tmp_path / "layout.c").write_text("\n".join(src) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", str(tmp_path / "layout.c"), "-o", str(exe)], check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.splitlines():
+        cname, what, val = line.split()
+        got[(cname, what)] = int(val)
+    for cname, cls in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(cls), cname
+        for fname, _ in cls._fields_:
+            assert got[(cname, fname)] == getattr(cls, fname).offset, (cname, fname)
+
+
 def test_fwd_rejects_bad_pointers():
     assert fwd(q=None) == fa.FA_ERR_NULL
     assert fwd(o=None) == fa.FA_ERR_NULL

@@ -273,3 +273,28 @@ def test_xcd_pinned_schedule(B, Hq, Hkv, S):
     (o, lse), o_ref, l_ref = run_case(B, Hq, Hkv, S, S, 128, "bf16", dict(mask=1), seed=B * S)
     check_out(o, o_ref, "bf16")
     check_lse(lse, l_ref)
+
+
+@pytest.mark.parametrize("S,rows", [(700, 128), (2600, 256)])
+def test_wg_trace_records(S, rows):
+    """fa_mask_params.wg_trace: one record per query tile of the static
+    schedule (128-row tiles up to 1024 keys, 256-row ping-pong tiles above),
+    end after start, the causal key-step count of each tile, an XCD id below
+    8; the output is the same bits as without the trace."""
+    B, Hq, Hkv, D = 2, 4, 2, 128
+    q, k, v = (dev(t) for t in synth.qkv(B, Hq, Hkv, S, S, D, 77))
+    o_ref = fa.forward(q, k, v, mask=1)
+    tr = fa.new_wg_trace(B, Hq, S)
+    o = fa.forward(q, k, v, mask=1, wg_trace=tr)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+    recs = fa.decode_wg_trace(tr.cpu().numpy())
+    n_tiles = B * Hq * -(-S // rows)
+    assert sorted(r["P"] for r in recs) == list(range(n_tiles))
+    steps_of_tile = {}
+    for t in range(-(-S // rows)):
+        steps_of_tile[t] = -(-min(S, (t + 1) * rows) // 64)
+    for r in recs:
+        assert r["end_us"] > r["start_us"] and r["rows"] == rows and 0 <= r["xcd"] < 8
+        assert r["steps"] in steps_of_tile.values()
+    assert sorted(r["steps"] for r in recs) == sorted(list(steps_of_tile.values()) * B * Hq)

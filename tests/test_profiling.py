@@ -137,3 +137,36 @@ def test_bench_tables(tmp_path, monkeypatch, which, name, rows):
              and not ln.startswith("| S |") and not ln.startswith("| run |")]
     assert len(table) == rows
     assert "python3 bench.py --workload" in open(path).read()
+
+
+def test_wgtrace_decode_and_stats(tmp_path, monkeypatch):
+    """Records of two compute units on XCDs 0 and 1, each running two
+    workgroups at once; tile time 2 us + 0.5 us per step."""
+    import numpy as np
+
+    from tiled_attention_fa_amd import binding
+    rec = np.zeros((8, binding.FA_WG_TRACE_WORDS), dtype=np.int64)
+    # P, start (us), steps, xcd, cu field (HW_ID bits 15:8)
+    plan = [(0, 0.0, 4, 0, 3), (2, 0.0, 8, 0, 3), (1, 0.0, 4, 1, 5), (3, 0.0, 2, 1, 5),
+            (4, 4.5, 2, 0, 3), (5, 3.5, 6, 1, 5)]
+    for p, t0, steps, xcd, cu in plan:
+        dur = 2.0 + 0.5 * steps
+        rec[p] = [int(t0 * 100), int((t0 + dur) * 100), (xcd << 32) | (cu << 8) | 0x3, (128 << 32) | steps]
+    recs = binding.decode_wg_trace(rec)
+    assert len(recs) == 6 and {r["P"] for r in recs} == {0, 1, 2, 3, 4, 5}  # unwritten records skipped
+    assert all(r["rows"] == 128 for r in recs) and {r["cu"] for r in recs} == {(0 << 8) | 3, (1 << 8) | 5}
+    st = profiling.wgtrace_stats(recs)
+    assert st["compute_units"] == 2 and st["per_cu_concurrency"] == 2
+    assert st["fit"]["fixed_us"] == pytest.approx(2.0) and st["fit"]["per_step_us"] == pytest.approx(0.5)
+    assert st["fit"]["r2"] == pytest.approx(1.0)
+    assert st["span_us"] == pytest.approx(8.5)  # P 5: 3.5 + 5
+    assert st["ideal_span_us"] == pytest.approx(sum(2.0 + 0.5 * s for _, _, s, _, _ in plan) / 4)
+    assert st["xcd_match"] == pytest.approx(sum(p % 8 == x for p, _, _, x, _ in plan) / len(plan))
+    assert st["gap_us"]["median"] == pytest.approx(0.5)  # P 4 starts 0.5 us after P 0 ends; P 5 at 0.5 after P 3
+    assert st["xcds"][0]["steps"] == 14 and st["xcds"][1]["steps"] == 12
+    d = tmp_path / "out" / "wgtrace"
+    d.mkdir(parents=True)
+    np.save(d / "gqa_causal.npy", rec)
+    monkeypatch.setattr(profiling, "PROFILES", str(tmp_path / "profiles"))
+    text = open(profiling.write_wgtrace_summary("gqa_causal", str(tmp_path / "out"))).read()
+    assert "--wg-trace" in text and "| 0 | 3 |" in text

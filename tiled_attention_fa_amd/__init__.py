@@ -16,4 +16,5 @@ from .binding import (  # noqa: F401
     fa_bwd_rel_bias_workspace_bytes, fa_block_mask_bytes, fa_fwd_kv_step,
     fa_status_str, fa_version, default_scale, build_block_mask, forward, backward,
     FP8_BLOCK, quantize_fp8, forward_fp8, FA_WORK_QUEUE_INTS, new_work_queue,
+    FA_WG_TRACE_WORDS, new_wg_trace, decode_wg_trace,
 )

@@ -36,7 +36,7 @@ EXPORTED = ("fa_fwd", "fa_fwd_kv_step", "fa_bwd", "fa_bwd_phase", "fa_bwd_noallo
 
 class FaMaskParams(ctypes.Structure):
     _fields_ = [("window", ctypes.c_int32), ("doc_ids", ctypes.c_void_p), ("visited", ctypes.c_void_p),
-                ("work_queue", ctypes.c_void_p)]
+                ("work_queue", ctypes.c_void_p), ("wg_trace", ctypes.c_void_p)]
 
 
 class FaModParams(ctypes.Structure):
@@ -234,9 +234,9 @@ def _dtype_code(t) -> int:
 
 
 def _params(mask, window, doc_ids, visited, mod, alibi_slopes, softcap, boost_radius, boost_factor,
-            rel_bias=None, rel_bias_grad=None, rel_bias_ws=None, work_queue=None):
+            rel_bias=None, rel_bias_grad=None, rel_bias_ws=None, work_queue=None, wg_trace=None):
     ptr = lambda t: None if t is None else t.data_ptr()
-    mp = FaMaskParams(int(window), ptr(doc_ids), ptr(visited), ptr(work_queue))
+    mp = FaMaskParams(int(window), ptr(doc_ids), ptr(visited), ptr(work_queue), ptr(wg_trace))
     ws_bytes = 0 if rel_bias_ws is None else rel_bias_ws.numel() * rel_bias_ws.element_size()
     op = FaModParams(ptr(alibi_slopes), float(softcap), int(boost_radius), float(boost_factor),
                      ptr(rel_bias), ptr(rel_bias_grad), ptr(rel_bias_ws), int(ws_bytes))
@@ -249,6 +249,29 @@ FA_WORK_QUEUE_INTS = 288
 def new_work_queue(device="cuda"):
     """A zeroed work queue for the persistent forward (fa_mask_params.work_queue)."""
     return _torch().zeros(FA_WORK_QUEUE_INTS, dtype=_torch().int32, device=device)
+
+
+FA_WG_TRACE_WORDS = 4
+
+
+def new_wg_trace(B, Hq, Sq, device="cuda"):
+    """A zeroed workgroup-trace buffer for fa_fwd (fa_mask_params.wg_trace)."""
+    return _torch().zeros((B * Hq * -(-Sq // BLOCK), FA_WG_TRACE_WORDS), dtype=_torch().int64, device=device)
+
+
+def decode_wg_trace(rec):
+    """Records of a wg_trace buffer (host array [n, 4]) as dicts, skipping the
+    entries no tile wrote: start/end in us of the 100 MHz clock, the XCD (XCC_ID
+    bits 3:0), a compute-unit key unique on the chip (XCD, and HW_ID bits 15:8:
+    CU, shader array and shader engine), the static index P, rows and steps."""
+    out = []
+    for p, (t0, t1, loc, size) in enumerate(rec.tolist()):
+        if t0 == 0 and t1 == 0:
+            continue
+        xcc, hw = (loc >> 32) & 0xF, loc & 0xFFFFFFFF
+        out.append({"P": p, "start_us": t0 / 100.0, "end_us": t1 / 100.0, "xcd": xcc,
+                    "cu": (xcc << 8) | ((hw >> 8) & 0xFF), "rows": size >> 32, "steps": size & 0xFFFFFFFF})
+    return out
 
 
 FP8_BLOCK = 128  # rows per FP8 quantization block
@@ -376,18 +399,23 @@ def build_block_mask(mask: int, B: int, Sq: int, Skv: int, *, window: int = 0, d
 
 def forward(q, k, v, *, scale=None, mask=MASK_NONE, window=0, doc_ids=None, mod=MOD_NONE,
             alibi_slopes=None, softcap=0.0, boost_radius=0, boost_factor=1.0, rel_bias=None,
-            block_mask=None, return_lse=False, out=None, lse=None, visited=None, work_queue=None, stream=None):
+            block_mask=None, return_lse=False, out=None, lse=None, visited=None, work_queue=None, wg_trace=None,
+            stream=None):
     """O (and LSE if ``return_lse``) for q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] on the GPU.
 
     ``rel_bias`` (MOD_REL_BIAS): float32 [Hq, Sq + Skv - 1] on the device.
     ``work_queue``: int32 [FA_WORK_QUEUE_INTS] on the device, zero before its
     first use (``new_work_queue()``): the persistent, dynamically scheduled
-    kernel takes its query tiles from it and leaves it zero."""
+    kernel takes its query tiles from it and leaves it zero.
+    ``wg_trace``: int64 [B * Hq * ceil(Sq / 128), FA_WG_TRACE_WORDS] on the
+    device (``new_wg_trace()``), debug records of where and when each query
+    tile ran."""
     torch = _torch()
     B, Hq, Hkv, Sq, Skv, D = _check_qkv(q, k, v)
     _check_mod_tensors(q, Hq, Sq, Skv, doc_ids, alibi_slopes, rel_bias)
     _dense(visited, "visited", None, (torch.int32,), q.device)
     _dense(work_queue, "work_queue", (FA_WORK_QUEUE_INTS,), (torch.int32,), q.device)
+    _dense(wg_trace, "wg_trace", (B * Hq * -(-Sq // BLOCK), FA_WG_TRACE_WORDS), (torch.int64,), q.device)
     if out is None:
         out = torch.empty((B, Hq, Sq, D), dtype=q.dtype, device=q.device)
     if return_lse and lse is None:
@@ -395,7 +423,7 @@ def forward(q, k, v, *, scale=None, mask=MASK_NONE, window=0, doc_ids=None, mod=
     _dense(out, "out", (B, Hq, Sq, D), (q.dtype,), q.device)
     _dense(lse if return_lse else None, "lse", (B, Hq, Sq), (torch.float32,), q.device)
     mp, op = _params(mask, window, doc_ids, visited, mod, alibi_slopes, softcap, boost_radius, boost_factor,
-                     rel_bias, work_queue=work_queue)
+                     rel_bias, work_queue=work_queue, wg_trace=wg_trace)
     bms = block_mask.struct() if block_mask is not None else None
     rc = fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse) if return_lse else None,
                 B, Hq, Hkv, Sq, Skv, D, _dtype_code(q), float(default_scale(D) if scale is None else scale),

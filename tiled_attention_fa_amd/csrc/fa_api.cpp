@@ -178,6 +178,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, i
   if (visited && !aligned(visited, 4)) return FA_ERR_ALIGN;
   int32_t* queue = mask_params ? mask_params->work_queue : nullptr;
   if (queue && !aligned(queue, 4)) return FA_ERR_ALIGN;
+  int64_t* trace = mask_params ? mask_params->wg_trace : nullptr;
+  if (trace && !aligned(trace, 8)) return FA_ERR_ALIGN;
   if (!has_q) return FA_OK;
   if (queue && device_cu_count(&a.n_cu) != hipSuccess) return FA_ERR_LAUNCH;
   a.queue = queue;
@@ -188,6 +190,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, i
   a.o = out;
   a.lse = lse;
   a.visited = visited;
+  a.trace = trace;
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;

@@ -65,6 +65,7 @@ struct FwdArgs {
   BlockMaskArgs bm;
   int32_t* queue;  // null: static schedule; else the work queue of a persistent launch
   int n_cu;        // compute units of the device (persistent grid size)
+  int64_t* trace;  // null, or FA_WG_TRACE_WORDS words per tile (debug)
 };
 
 // FP8 forward: E4M3 tensors with one E8M0 scale byte per 128-row block of

@@ -275,6 +275,34 @@ __device__ __forceinline__ void decode_work(int P, int B, int Hq, int Hkv, int n
   tile = heavy_first ? (n_tiles - 1 - r) : r;
 }
 
+// ---------------------------------------------------------------- workgroup trace
+// Debug records of fa_mask_params.wg_trace (kernels of the static schedule):
+// the constant-rate clock at a tile's start (read into scalar registers
+// when the tile starts) and end, where it ran (the XCC_ID and HW_ID
+// hardware registers, read with s_getreg: id 20 and id 4, all 32 bits) and
+// its size, all four words written at the end by lane 0 of the workgroup's
+// first wave (`first`: a wave-uniform test, so no thread index stays live
+// through the tile).  Plain vector stores; nothing when `tr` is null or
+// P < 0.
+__device__ __forceinline__ uint64_t trace_clock(const int64_t* tr) {
+  return tr != nullptr ? __builtin_amdgcn_s_memrealtime() : 0;
+}
+
+__device__ __forceinline__ void trace_end(int64_t* tr, int P, uint64_t t0, bool first, int rows, int steps) {
+  if (tr == nullptr || P < 0 || !first) return;
+  const unsigned lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  if (lane == 0) {
+    int64_t* e = tr + (size_t)P * FA_WG_TRACE_WORDS;
+    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+    const uint32_t xcc = (uint32_t)__builtin_amdgcn_s_getreg((31 << 11) | 20);
+    const uint32_t hw = (uint32_t)__builtin_amdgcn_s_getreg((31 << 11) | 4);
+    e[0] = (int64_t)t0;
+    e[1] = (int64_t)t1;
+    e[2] = (int64_t)(((uint64_t)xcc << 32) | hw);
+    e[3] = (int64_t)(((uint64_t)(uint32_t)rows << 32) | (uint32_t)steps);
+  }
+}
+
 // ---------------------------------------------------------------- work queue
 // Persistent kernels take the static schedule's workgroup indices P from a
 // queue of counters in caller memory (int32[kQueueInts], zero at launch).

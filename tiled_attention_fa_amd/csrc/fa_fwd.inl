@@ -190,7 +190,8 @@ struct FwdSmem {
 // step's loads are issued (persistent kernels take their next tile there, so
 // the queue's latency hides behind the step).
 template <int D, bool F32, int MASK, int MOD, bool BM, typename AtLast>
-__device__ __forceinline__ void fwd_tile(const FwdArgs& a, int b, int hq, int qt, AtLast at_last_step) {
+__device__ __forceinline__ void fwd_tile(const FwdArgs& a, int P, uint64_t t0, int b, int hq, int qt,
+                                         AtLast at_last_step) {
   using Cfg = FwdCfg<F32>;
   using Sm = FwdSmem<D, F32>;
   constexpr int BN = Cfg::BN, NT = Cfg::NT;
@@ -572,6 +573,7 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs& a, int b, int hq, int qt
       a.lse[(size_t)(b * a.Hq + hq) * Sq + qi] = lt > 0.0f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 + lse_shift : kNegInf;
   }
   if (a.visited != nullptr && tid == 0) atomicAdd(&a.visited[(size_t)(b * a.Hq + hq) * a.n_qt + qt], visited);
+  trace_end(a.trace, P, t0, wave == 0, kTileQ, n_steps);
 }
 
 // Query tile of the static schedule's workgroup P: XCD-pinned (batch, kv
@@ -586,9 +588,10 @@ __device__ __forceinline__ void fwd_tile_of(const FwdArgs& a, int P, int& b, int
 
 template <int D, bool F32, int MASK, int MOD, bool BM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(FwdArgs a) {
+  const uint64_t t0 = trace_clock(a.trace);
   int b, hq, qt;
   fwd_tile_of<MASK, BM>(a, blockIdx.x, b, hq, qt);
-  fwd_tile<D, F32, MASK, MOD, BM>(a, b, hq, qt, [] {});
+  fwd_tile<D, F32, MASK, MOD, BM>(a, blockIdx.x, t0, b, hq, qt, [] {});
 }
 
 // Persistent, dynamically scheduled form of fwd_kernel (the role of a
@@ -613,7 +616,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // The next tile's index is taken (thread 0) when this tile's last step
     // starts and read after the tile, when the step's loads have landed.
     int i_next = -1;
-    fwd_tile<D, F32, MASK, MOD, BM>(a, b, hq, qt, [&] {
+    fwd_tile<D, F32, MASK, MOD, BM>(a, -1, 0, b, hq, qt, [&] {
       if (threadIdx.x == 0) i_next = take_home(a.queue, wq, home);
     });
     P = finish_pull(a.queue, wq, home, i_next, &sUnit);
@@ -652,6 +655,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Relative-bias diagonals of one key step: QT + BN - 1 entries (5 chunks of 64).
   __shared__ __attribute__((aligned(16))) float sB0[REL ? 320 : 1], sB1[REL ? 320 : 1];
 
+  const uint64_t t0 = trace_clock(a.trace);
   int b, hq, qt;
   decode_work(blockIdx.x, a.B, a.Hq, a.Hkv, (a.Sq + QT - 1) / QT, MASK == MASK_CAUSAL, b, hq, qt);
   const int hk = hq / a.G;
@@ -860,6 +864,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     atomicAdd(&a.visited[(size_t)(b * a.Hq + hq) * a.n_qt + qg0 / kTileQ], vis);
   }
+  trace_end(a.trace, blockIdx.x, t0, wave == 0, QT, n_steps);
 }
 
 template <int D, int MASK>

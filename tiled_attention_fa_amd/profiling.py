@@ -32,6 +32,15 @@ instruction mix and shader clock, summarised into profiles/.
         schedule, recomputed against stored dS for dQ, each twice, in
         alternation: schedule_and_dq_variants.md).
 
+    python -m tiled_attention_fa_amd.profiling wgtrace --workload W --out DIR
+    python -m tiled_attention_fa_amd.profiling wgtrace-summary --workload W --out DIR
+        bench.py --wg-trace (no profiler): after the timed steps, one more
+        step whose forward records every query tile's start and end (the
+        100 MHz clock), compute unit and size; then
+        profiles/W_wgtrace.md: span, balance over compute units and XCDs,
+        the gaps between workgroups, and the fit duration = fixed + per
+        step x steps.
+
 Kernels are grouped by the bench.py timing keys (fwd, bwd_delta, bwd_dkdv,
 bwd_dq, block_mask).  Durations and counters are taken over the dispatches
 of bench.py's timed steps (a kernel launched once per step: its last 20).
@@ -441,9 +450,125 @@ def write_bench_table(which: str, out: str) -> str:
     return path
 
 
+# ---------------------------------------------------------------- workgroup traces
+def run_wgtrace(workload: str, out: str, limit: int, shape=(0, 0)) -> str:
+    d = os.path.join(os.path.abspath(out), "wgtrace")
+    os.makedirs(d, exist_ok=True)
+    path = os.path.join(d, label(workload, shape) + ".npy")
+    args = _bench_args(workload, BENCH_STEPS, BENCH_WARMUP, shape) + ["--wg-trace", path]
+    print(f"wgtrace: {label(workload, shape)}", flush=True)
+    r = subprocess.run(["timeout", "-s", "KILL", str(limit), *args], cwd=ROOT, stdout=subprocess.PIPE,
+                       stderr=subprocess.STDOUT, text=True)
+    with open(os.path.join(d, label(workload, shape) + ".log"), "w") as f:
+        f.write(r.stdout)
+    if r.returncode != 0:
+        sys.exit(f"bench.py --wg-trace for {workload} ended with status {r.returncode}")
+    return path
+
+
+def _quantile(xs: list, q: float) -> float:
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, int(q * (len(xs) - 1) + 0.5))]
+
+
+def wgtrace_stats(recs: list[dict]) -> dict:
+    """Balance and cost figures of one traced launch (records of
+    binding.decode_wg_trace)."""
+    t_min = min(r["start_us"] for r in recs)
+    span = max(r["end_us"] for r in recs) - t_min
+    dur = [r["end_us"] - r["start_us"] for r in recs]
+    by_cu: dict[int, list[dict]] = {}
+    for r in recs:
+        by_cu.setdefault(r["cu"], []).append(r)
+    # Workgroups resident on a compute unit at once (the launch's occupancy).
+    conc = 1
+    gaps = []
+    cu_end = []
+    for tiles in by_cu.values():
+        ev = sorted([(t["start_us"], 1) for t in tiles] + [(t["end_us"], -1) for t in tiles], key=lambda e: (e[0], e[1]))
+        c = 0
+        for _, d in ev:
+            c += d
+            conc = max(conc, c)
+        ends = sorted(t["end_us"] for t in tiles)
+        for t in tiles:  # time from the last end before this start (a freed slot) to this start
+            prev = [e for e in ends if e <= t["start_us"]]
+            if prev:
+                gaps.append(t["start_us"] - prev[-1])
+        cu_end.append(max(ends) - t_min)
+    ideal = sum(dur) / (len(by_cu) * conc)
+    # Least squares: duration = fixed + per_step * steps.
+    n = len(recs)
+    sx = sum(r["steps"] for r in recs)
+    sy = sum(dur)
+    sxx = sum(r["steps"] ** 2 for r in recs)
+    sxy = sum(r["steps"] * d for r, d in zip(recs, dur))
+    den = n * sxx - sx * sx
+    per_step = (n * sxy - sx * sy) / den if den else 0.0
+    fixed = (sy - per_step * sx) / n
+    ss_tot = sum((d - sy / n) ** 2 for d in dur)
+    ss_res = sum((d - fixed - per_step * r["steps"]) ** 2 for r, d in zip(recs, dur))
+    xcds = {}
+    for r, d in zip(recs, dur):
+        x = xcds.setdefault(r["xcd"], {"tiles": 0, "busy_us": 0.0, "steps": 0, "end_us": 0.0})
+        x["tiles"] += 1
+        x["busy_us"] += d
+        x["steps"] += r["steps"]
+        x["end_us"] = max(x["end_us"], r["end_us"] - t_min)
+    for x in xcds.values():
+        x["us_per_step"] = x["busy_us"] / max(1, x["steps"])
+    return {"tiles": n, "rows": recs[0]["rows"], "span_us": span, "compute_units": len(by_cu),
+            "per_cu_concurrency": conc, "ideal_span_us": ideal,
+            "cu_end_us": {"min": min(cu_end), "median": _quantile(cu_end, 0.5), "max": max(cu_end)},
+            "gap_us": {"median": _quantile(gaps, 0.5), "p90": _quantile(gaps, 0.9), "n": len(gaps)} if gaps else None,
+            "fit": {"fixed_us": fixed, "per_step_us": per_step, "r2": 1 - ss_res / ss_tot if ss_tot else 1.0},
+            "xcd_match": sum(1 for r in recs if r["xcd"] == r["P"] % 8) / n,
+            "xcds": dict(sorted(xcds.items()))}
+
+
+def write_wgtrace_summary(workload: str, out: str, shape=(0, 0)) -> str:
+    import numpy as np
+    from . import binding
+    lab = label(workload, shape)
+    recs = binding.decode_wg_trace(np.load(os.path.join(out, "wgtrace", lab + ".npy")))
+    st = wgtrace_stats(recs)
+    args = _bench_args(workload, BENCH_STEPS, BENCH_WARMUP, shape)
+    cmd = " ".join("python3" if x == sys.executable else x for x in args).replace(ROOT, "<repo>")
+    f = st["fit"]
+    lines = [f"# Workgroup trace of the forward: {lab}", "",
+             "Command (repository root on the GPU host; `python -m tiled_attention_fa_amd.profiling wgtrace` runs it):",
+             "", "```", cmd + " --wg-trace <out>/wgtrace/" + lab + ".npy", "```", "",
+             "After the timed steps, one more step runs with fa_mask_params.wg_trace: every query tile records "
+             "the GPU's 100 MHz clock at its start and end, its compute unit (XCC_ID, HW_ID) and its key steps.",
+             "", "| figure | value |", "|---|---|",
+             f"| tiles ({st['rows']} query rows each) | {st['tiles']} |",
+             f"| compute units seen, workgroups resident per unit | {st['compute_units']}, {st['per_cu_concurrency']} |",
+             f"| span, first start to last end (us) | {st['span_us']:.1f} |",
+             f"| ideal span: summed tile time / (units x resident) (us) | {st['ideal_span_us']:.1f} "
+             f"({st['ideal_span_us'] / st['span_us']:.3f} of the span) |",
+             f"| last end per compute unit, min / median / max (us) | {st['cu_end_us']['min']:.1f} / "
+             f"{st['cu_end_us']['median']:.1f} / {st['cu_end_us']['max']:.1f} |"]
+    if st["gap_us"]:
+        lines.append(f"| slot freed to next start on that unit, median / p90 (us; {st['gap_us']['n']} starts) | "
+                     f"{st['gap_us']['median']:.2f} / {st['gap_us']['p90']:.2f} |")
+    lines += [f"| tile duration = fixed + per step x steps: fixed, per step (us), R^2 | {f['fixed_us']:.2f}, "
+              f"{f['per_step_us']:.3f}, {f['r2']:.3f} |",
+              f"| tiles whose XCD is their schedule index mod 8 | {st['xcd_match']:.3f} |", "",
+              "| XCD | tiles | summed tile time (us) | key steps | us per step | last end (us) |",
+              "|---|---|---|---|---|---|"]
+    for x, v in st["xcds"].items():
+        lines.append(f"| {x} | {v['tiles']} | {v['busy_us']:.0f} | {v['steps']} | {v['us_per_step']:.3f} | "
+                     f"{v['end_us']:.1f} |")
+    path = os.path.join(PROFILES, f"{lab}_wgtrace.md")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return path
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("action", choices=["run", "summarize", "bench", "bench-summary"])
+    ap.add_argument("action", choices=["run", "summarize", "bench", "bench-summary", "wgtrace", "wgtrace-summary"])
     ap.add_argument("--workload")
     ap.add_argument("--set", choices=["workloads", "seqlen", "variants"])
     ap.add_argument("--out", required=True)
@@ -462,6 +587,12 @@ def main() -> None:
         return
     if not args.workload:
         ap.error("--workload is required")
+    if args.action == "wgtrace":
+        run_wgtrace(args.workload, args.out, max(args.limit, 300), shape)
+        return
+    if args.action == "wgtrace-summary":
+        print(write_wgtrace_summary(args.workload, args.out, shape))
+        return
     if args.action == "run":
         run(args.workload, args.out, args.limit, shape)
     else:
