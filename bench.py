@@ -254,7 +254,8 @@ def main():
                          "(fa_mask_params.work_queue)")
     ap.add_argument("--wg-trace", default="", metavar="FILE.npy",
                     help="after the timed steps, run one more step whose forward records each query tile's "
-                         "start, end, compute unit and size (fa_mask_params.wg_trace) and save the records")
+                         "start, end, compute unit and size (fa_mask_params.wg_trace) and save the records; "
+                         "with a backward, its dK/dV and dQ records go to FILE.bwd.npy")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (3 times) and exit: the reference for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -344,12 +345,13 @@ def main():
             evs[i].record(stream)
         if w.backward:
             for ph in (fa.FA_BWD_DELTA, fa.FA_BWD_DKDV, fa.FA_BWD_DQ):
-                fa.backward(q, k, v, out, do, lse, block_mask=bm, workspace=ws, grads=grads, phases=ph, **kw)
+                fa.backward(q, k, v, out, do, lse, block_mask=bm, workspace=ws, grads=grads, phases=ph,
+                            wg_trace=trace_buf[1], **kw)
                 i += 1
                 if evs:
                     evs[i].record(stream)
 
-    trace_buf = [None]  # set for the one traced step after the timed ones (--wg-trace)
+    trace_buf = [None, None]  # forward, backward: set for the one traced step after the timed ones
     for _ in range(args.warmup):
         step(None)
     torch.cuda.synchronize()
@@ -371,10 +373,15 @@ def main():
             sys.exit("--wg-trace covers the bf16/fp32 forward with the static schedule")
         import numpy as np
         trace_buf[0] = fa.new_wg_trace(w.B, w.Hq, w.S, dev)
+        if w.backward:
+            trace_buf[1] = fa.new_wg_trace(w.B, w.Hq, w.S, dev, Hkv=w.Hkv, Skv=w.S)
         step(None)
         torch.cuda.synchronize()
         np.save(args.wg_trace, trace_buf[0].cpu().numpy())
-        trace_buf[0] = None
+        if w.backward:  # dK/dV records, then dQ records
+            np.save(args.wg_trace[:-4] + ".bwd.npy" if args.wg_trace.endswith(".npy") else args.wg_trace + ".bwd.npy",
+                    trace_buf[1].cpu().numpy())
+        trace_buf[0] = trace_buf[1] = None
     per_step = {n: sorted(e[i].elapsed_time(e[i + 1]) for e in evs) for i, n in enumerate(names)}
     kernel_ms = {n: sum(t) / args.steps for n, t in per_step.items()}
 

@@ -119,7 +119,13 @@ typedef struct {
                               HW_ID register of the workgroup's first wave,
                               [3] the tile's query rows << 32 | its key
                               steps.  Static schedule only: ignored with a
-                              work_queue, and by fa_bwd.  NULL in production. */
+                              work_queue.  fa_bwd (all its forms) writes the
+                              same records for its dK/dV workgroups (key
+                              tiles: [3] holds 128 << 32 | the query steps)
+                              at 0 <= P < B * Hkv * ceil(Skv/128), then for
+                              its dQ workgroups from that index on (room:
+                              B * Hkv * ceil(Skv/128) + B * Hq * ceil(Sq/128)
+                              records).  NULL in production. */
 } fa_mask_params;
 
 /* Words per record of fa_mask_params.wg_trace. */

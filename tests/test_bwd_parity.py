@@ -199,3 +199,34 @@ def test_xcd_pinned_schedule(B, Hq, Hkv, S):
     got, ref = run_bwd(B, Hq, Hkv, S, 128, dict(mask=1), seed=B * S + 1)
     for g, r, what in zip(got, ref, ("dQ", "dK", "dV")):
         check_out(g, r, "bf16", what)
+
+
+def test_wg_trace_records():
+    """fa_mask_params.wg_trace in the backward: one record per dK/dV
+    workgroup (key tiles), then one per dQ workgroup, each with its query
+    or key step count; the gradients are the same bits as without it."""
+    B, Hq, Hkv, S, D = 2, 4, 2, 700, 128
+    q, k, v = (dev(t) for t in synth.qkv(B, Hq, Hkv, S, S, D, 78))
+    do = dev(synth.randn((B, Hq, S, D), 79))
+    o, lse = fa.forward(q, k, v, mask=1, return_lse=True)
+    ref = fa.backward(q, k, v, o, do, lse, mask=1)
+    tr = fa.new_wg_trace(B, Hq, S, Hkv=Hkv, Skv=S)
+    got = fa.backward(q, k, v, o, do, lse, mask=1, wg_trace=tr)
+    torch.cuda.synchronize()
+    for x, y in zip(got, ref):
+        assert torch.equal(x, y)
+    rec = tr.cpu().numpy()
+    n_t = -(-S // 128)
+    n_kv = B * Hkv * n_t
+    kv = fa.decode_wg_trace(rec[:n_kv])
+    dq = fa.decode_wg_trace(rec[n_kv:])
+    assert sorted(r["P"] for r in kv) == list(range(n_kv))
+    assert sorted(r["P"] for r in dq) == list(range(B * Hq * n_t))
+    # Causal: key tile kt visits the 32-row query steps from 4 kt on, for
+    # each of the G = 2 query heads; query tile qt the 64-key steps up to it.
+    n_qs = -(-S // 32)
+    want_kv = sorted([2 * (n_qs - 4 * t) for t in range(n_t)] * (B * Hkv))
+    want_dq = sorted([-(-min(S, 128 * (t + 1)) // 64) for t in range(n_t)] * (B * Hq))
+    assert sorted(r["steps"] for r in kv) == want_kv
+    assert sorted(r["steps"] for r in dq) == want_dq
+    assert all(r["end_us"] > r["start_us"] and 0 <= r["xcd"] < 8 for r in kv + dq)

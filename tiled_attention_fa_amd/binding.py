@@ -254,9 +254,13 @@ def new_work_queue(device="cuda"):
 FA_WG_TRACE_WORDS = 4
 
 
-def new_wg_trace(B, Hq, Sq, device="cuda"):
-    """A zeroed workgroup-trace buffer for fa_fwd (fa_mask_params.wg_trace)."""
-    return _torch().zeros((B * Hq * -(-Sq // BLOCK), FA_WG_TRACE_WORDS), dtype=_torch().int64, device=device)
+def new_wg_trace(B, Hq, Sq, device="cuda", Hkv=None, Skv=None):
+    """A zeroed workgroup-trace buffer (fa_mask_params.wg_trace): for fa_fwd,
+    or with Hkv and Skv given for fa_bwd (dK/dV records, then dQ records)."""
+    n = B * Hq * -(-Sq // BLOCK)
+    if Hkv is not None:
+        n += B * Hkv * -(-(Skv if Skv is not None else Sq) // BLOCK)
+    return _torch().zeros((n, FA_WG_TRACE_WORDS), dtype=_torch().int64, device=device)
 
 
 def decode_wg_trace(rec):
@@ -438,7 +442,7 @@ def backward(q, k, v, out, dout, lse, *, scale=None, mask=MASK_NONE, window=0, d
              mod=MOD_NONE, alibi_slopes=None, softcap=0.0, boost_radius=0, boost_factor=1.0,
              rel_bias=None, rel_bias_grad=None, rel_bias_ws=None,
              block_mask=None, workspace=None, grads=None, stream=None,
-             phases=FA_BWD_DELTA | FA_BWD_DKDV | FA_BWD_DQ, noalloc=False, store_ds=False):
+             phases=FA_BWD_DELTA | FA_BWD_DKDV | FA_BWD_DQ, noalloc=False, store_ds=False, wg_trace=None):
     """(dq, dk, dv) of sum(O * dout), recomputing P from ``lse``.
 
     ``phases`` selects which of the three backward launches run (all by
@@ -450,7 +454,9 @@ def backward(q, k, v, out, dout, lse, *, scale=None, mask=MASK_NONE, window=0, d
     stores (unmasked and causal attention).  With MOD_REL_BIAS, ``rel_bias_grad`` (float32
     [Hq, Sq + Skv - 1], or True to allocate it) receives the gradient of the
     bias table; its scratch ``rel_bias_ws`` is allocated when not given.  The
-    return value is then (dq, dk, dv, rel_bias_grad)."""
+    return value is then (dq, dk, dv, rel_bias_grad).  ``wg_trace``
+    (``new_wg_trace(B, Hq, Sq, Hkv=Hkv, Skv=Skv)``): debug records of the
+    dK/dV and dQ workgroups."""
     torch = _torch()
     B, Hq, Hkv, Sq, Skv, D = _check_qkv(q, k, v)
     _check_mod_tensors(q, Hq, Sq, Skv, doc_ids, alibi_slopes, rel_bias)
@@ -482,8 +488,10 @@ def backward(q, k, v, out, dout, lse, *, scale=None, mask=MASK_NONE, window=0, d
                                   device=q.device)
     _dense(rel_bias_grad, "rel_bias_grad", (Hq, Sq + Skv - 1), (torch.float32,), q.device)
     _dense(rel_bias_ws, "rel_bias_ws", None, None, q.device)
+    _dense(wg_trace, "wg_trace", (B * Hkv * -(-Skv // BLOCK) + B * Hq * -(-Sq // BLOCK), FA_WG_TRACE_WORDS),
+           (torch.int64,), q.device)
     mp, op = _params(mask, window, doc_ids, None, mod, alibi_slopes, softcap, boost_radius, boost_factor,
-                     rel_bias, rel_bias_grad, rel_bias_ws)
+                     rel_bias, rel_bias_grad, rel_bias_ws, wg_trace=wg_trace)
     bms = block_mask.struct() if block_mask is not None else None
     tail = (B, Hq, Hkv, Sq, Skv, D, _dtype_code(q), float(default_scale(D) if scale is None else scale),
             int(mask), ctypes.byref(mp), int(mod), ctypes.byref(op),

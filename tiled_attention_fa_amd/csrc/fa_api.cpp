@@ -344,9 +344,12 @@ static int bwd_entry(int phase, const void* q, const void* k, const void* v, con
     }
     a.mod.rel_bias_grad = mod_params->rel_bias_grad;
   }
+  int64_t* trace = mask_params ? mask_params->wg_trace : nullptr;
+  if (trace && !aligned(trace, 8)) return FA_ERR_ALIGN;
   if (B == 0 && !bias_grad) return FA_OK;
   if (use_scratch && scratch_address(&workspace) != hipSuccess) return FA_ERR_LAUNCH;
 
+  a.trace = trace;
   a.q = q;
   a.k = k;
   a.v = v;

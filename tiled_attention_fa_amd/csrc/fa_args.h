@@ -109,6 +109,9 @@ struct BwdArgs {
   uint16_t* ds;
   long ds_blocks;
   int n_qs;  // query steps of 32 rows
+  // Debug records (fa_mask_params.wg_trace): the dK/dV workgroups' first,
+  // then the dQ workgroups' from record B * Hkv * n_kt on.
+  int64_t* trace;
 };
 
 // Elements of one stored dS block: 4 waves x 64 lanes x 16 bf16.

@@ -106,6 +106,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr bool REL = MOD == MOD_REL_BIAS;
   __shared__ __attribute__((aligned(16))) float sB0[REL ? 192 : 1], sB1[REL ? 192 : 1];
 
+  const uint64_t t0 = trace_clock(a.trace);
   int b, hk, kt;
   decode_work(blockIdx.x, a.B, a.Hkv, a.Hkv, a.n_kt, false, b, hk, kt);
   if constexpr (BM) kt = ordered_tile(a.bm.kv_order, a.bm.n_b, b, a.bm.n_kv, kt, kt);
@@ -345,6 +346,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                    pack_bf16(dv[dt][4 * rq + 2], dv[dt][4 * rq + 3])};
       }
   }
+  trace_end(a.trace, blockIdx.x, t0, wave == 0, BK, n_steps);
 }
 
 // ---------------------------------------------------------------- dQ
@@ -376,6 +378,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int GS = 96;
   __shared__ __attribute__((aligned(16))) float sG[REL ? 2 * 8 * GS : 1], sRing[REL ? 256 : 1];
 
+  const uint64_t t0 = trace_clock(a.trace);
   int b, hq, qt;
   decode_work(blockIdx.x, a.B, a.Hq, a.Hkv, a.n_qt,
               (MASK == MASK_CAUSAL || MASK == MASK_DOCUMENT) && !(BM && a.bm.q_order), b, hq, qt);
@@ -631,6 +634,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                    pack_bf16(dq[dt][4 * rq + 2] * a.scale, dq[dt][4 * rq + 3] * a.scale)};
       }
   }
+  trace_end(a.trace == nullptr ? nullptr : a.trace + (size_t)a.B * a.Hkv * a.n_kt * FA_WG_TRACE_WORDS, blockIdx.x,
+            t0, wave == 0, kTileQ, n_steps);
 }
 
 // ---------------------------------------------------------------- dQ from stored dS
@@ -653,6 +658,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(16))) char sK0[TILE], sK1[TILE];
   __shared__ __attribute__((aligned(16))) char sS0[4 * SWAVE], sS1[4 * SWAVE];
 
+  const uint64_t t0 = trace_clock(a.trace);
   int b, hq, qt;
   decode_work(blockIdx.x, a.B, a.Hq, a.Hkv, a.n_qt, MASK == MASK_CAUSAL, b, hq, qt);
   const int hk = hq / a.G;
@@ -743,6 +749,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                    pack_bf16(dq[dt][4 * rq + 2] * a.scale, dq[dt][4 * rq + 3] * a.scale)};
       }
   }
+  trace_end(a.trace == nullptr ? nullptr : a.trace + (size_t)a.B * a.Hkv * a.n_kt * FA_WG_TRACE_WORDS, blockIdx.x,
+            t0, wave == 0, kTileQ, n_steps);
 }
 
 // ---------------------------------------------------------------- bias gradient

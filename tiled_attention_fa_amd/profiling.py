@@ -526,22 +526,10 @@ def wgtrace_stats(recs: list[dict]) -> dict:
             "xcds": dict(sorted(xcds.items()))}
 
 
-def write_wgtrace_summary(workload: str, out: str, shape=(0, 0)) -> str:
-    import numpy as np
-    from . import binding
-    lab = label(workload, shape)
-    recs = binding.decode_wg_trace(np.load(os.path.join(out, "wgtrace", lab + ".npy")))
-    st = wgtrace_stats(recs)
-    args = _bench_args(workload, BENCH_STEPS, BENCH_WARMUP, shape)
-    cmd = " ".join("python3" if x == sys.executable else x for x in args).replace(ROOT, "<repo>")
+def _wgtrace_table(title: str, st: dict, unit: str) -> list[str]:
     f = st["fit"]
-    lines = [f"# Workgroup trace of the forward: {lab}", "",
-             "Command (repository root on the GPU host; `python -m tiled_attention_fa_amd.profiling wgtrace` runs it):",
-             "", "```", cmd + " --wg-trace <out>/wgtrace/" + lab + ".npy", "```", "",
-             "After the timed steps, one more step runs with fa_mask_params.wg_trace: every query tile records "
-             "the GPU's 100 MHz clock at its start and end, its compute unit (XCC_ID, HW_ID) and its key steps.",
-             "", "| figure | value |", "|---|---|",
-             f"| tiles ({st['rows']} query rows each) | {st['tiles']} |",
+    lines = [f"## {title}", "", "| figure | value |", "|---|---|",
+             f"| tiles ({st['rows']} {unit} each) | {st['tiles']} |",
              f"| compute units seen, workgroups resident per unit | {st['compute_units']}, {st['per_cu_concurrency']} |",
              f"| span, first start to last end (us) | {st['span_us']:.1f} |",
              f"| ideal span: summed tile time / (units x resident) (us) | {st['ideal_span_us']:.1f} "
@@ -554,15 +542,43 @@ def write_wgtrace_summary(workload: str, out: str, shape=(0, 0)) -> str:
     lines += [f"| tile duration = fixed + per step x steps: fixed, per step (us), R^2 | {f['fixed_us']:.2f}, "
               f"{f['per_step_us']:.3f}, {f['r2']:.3f} |",
               f"| tiles whose XCD is their schedule index mod 8 | {st['xcd_match']:.3f} |", "",
-              "| XCD | tiles | summed tile time (us) | key steps | us per step | last end (us) |",
+              "| XCD | tiles | summed tile time (us) | steps | us per step | last end (us) |",
               "|---|---|---|---|---|---|"]
     for x, v in st["xcds"].items():
         lines.append(f"| {x} | {v['tiles']} | {v['busy_us']:.0f} | {v['steps']} | {v['us_per_step']:.3f} | "
                      f"{v['end_us']:.1f} |")
+    return lines + [""]
+
+
+def write_wgtrace_summary(workload: str, out: str, shape=(0, 0)) -> str:
+    import numpy as np
+    from . import binding
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import synth  # the workload shapes only
+    lab = label(workload, shape)
+    base = os.path.join(out, "wgtrace", lab)
+    args = _bench_args(workload, BENCH_STEPS, BENCH_WARMUP, shape)
+    cmd = " ".join("python3" if x == sys.executable else x for x in args).replace(ROOT, "<repo>")
+    lines = [f"# Workgroup traces: {lab}", "",
+             "Command (repository root on the GPU host; `python -m tiled_attention_fa_amd.profiling wgtrace` runs it):",
+             "", "```", cmd + " --wg-trace <out>/wgtrace/" + lab + ".npy", "```", "",
+             "After the timed steps, one more step runs with fa_mask_params.wg_trace: every workgroup records "
+             "the GPU's 100 MHz clock at its start and end, its compute unit (XCC_ID, HW_ID) and its steps "
+             "(forward: key steps of 64 keys; dK/dV: query steps of 32 rows; dQ: key steps of 64 keys).", ""]
+    lines += _wgtrace_table("Forward", wgtrace_stats(binding.decode_wg_trace(np.load(base + ".npy"))), "query rows")
+    if os.path.exists(base + ".bwd.npy"):
+        w = synth.WORKLOADS[workload]
+        B, S = shape[0] or w.B, shape[1] or w.S
+        n_kv = B * w.Hkv * -(-S // binding.BLOCK)
+        rec = np.load(base + ".bwd.npy")
+        lines += _wgtrace_table("Backward dK/dV", wgtrace_stats(binding.decode_wg_trace(rec[:n_kv])), "keys")
+        dq = binding.decode_wg_trace(rec[n_kv:])
+        lines += _wgtrace_table("Backward dQ", wgtrace_stats(dq), "query rows")
     path = os.path.join(PROFILES, f"{lab}_wgtrace.md")
     os.makedirs(PROFILES, exist_ok=True)
     with open(path, "w") as fh:
-        fh.write("\n".join(lines) + "\n")
+        fh.write("\n".join(lines))
     return path
 
 
