@@ -80,6 +80,15 @@ __device__ __forceinline__ u32x4 pack8(const f32x16& v, int base) {
                pack_bf16(v[base + 4], v[base + 5]), pack_bf16(v[base + 6], v[base + 7])};
 }
 
+// The dK/dV and dQ steps issue their LDS operand reads ahead of the matrix
+// products (scheduling groups) where the registers allow it: every variant
+// but the document mask, the relative bias, and local boost over a block
+// mask, which would spill with the extra fragments in flight.
+template <int MASK, int MOD, bool BM>
+constexpr bool bwd_read_ahead() {
+  return MASK != MASK_DOCUMENT && MOD != MOD_REL_BIAS && !(BM && MOD == MOD_BOOST);
+}
+
 // ---------------------------------------------------------------- dK, dV
 // Workgroup: 4 waves own keys [k0, k0 + 128), 32 per wave (one key column
 // per lane).  K rows stay in registers; the workgroup's 128 V rows sit in
@@ -241,6 +250,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int o = qrow ^ (32 * c);
         sp = mfma_bf16(*(const u32x4*)(qs + o), kf[c], sp);
         dp = mfma_bf16(*(const u32x4*)(ds + o), *(const u32x4*)(vw + o), dp);
+      }
+      // LDS operands read ahead of the matrix products: 4 reads first, then
+      // per pair of products the next three (Q, dO, V of the next chunk).
+      if constexpr (bwd_read_ahead<MASK, MOD, BM>()) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < KC - 2; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
       }
       // P and dS (register r: query q0 + 8(r/4) + 4hh + r%4).  Full tiles
       // take a branch without the mask test.  bl[8 rq + e] is the bias of
@@ -547,6 +571,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           st = mfma_bf16(*(const u32x4*)(ks + o), qf[c], st);
           dpt = mfma_bf16(*(const u32x4*)(vs + o), of[c], dpt);
         }
+        // K and V fragments read four products ahead.
+        if constexpr (bwd_read_ahead<MASK, MOD, BM>()) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+          for (int i = 0; i < 2 * KC - 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
         // Full tiles take a branch without the mask test.
         auto pds = [&](auto masked) {
           constexpr bool MASKED = decltype(masked)::value;
@@ -584,6 +618,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const u32x2 hi = lds_read_tr16(ks + ((t1 ^ (64 * dt)) + rows));
             dq[dt] = mfma_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, cc ? sb1 : sb0, dq[dt]);
           }
+        // Transposing K reads two products ahead.
+        if constexpr (bwd_read_ahead<MASK, MOD, BM>()) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+          for (int i = 0; i < 2 * DT - 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
       }
     }
     wait_loads();
