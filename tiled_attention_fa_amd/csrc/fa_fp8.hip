@@ -228,6 +228,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           st[t] = mfma_fp8(kf, qf[c], st[t], skb, sq);
         }
       }
+      // ---- V^T fragments of the whole step, read before the softmax so their
+      // latency hides behind it.  A-operand byte p of a lane is V[kappa(hh, p)][d].
+      i32x8 vf[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int qv = 0; qv < 4; ++qv) {
+          const int pk = 8 * qv + (L >> 1);                 // k-slot this lane addresses
+          const int key = 32 * (pk >> 4) + 8 * ((pk & 15) >> 2) + 4 * hh + (pk & 3);
+          const int ch = 2 * dt + g16;
+          const char* addr = vs + key * D + swz8<D>(key, ch) * 16 + 8 * (L & 1);
+          typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+          const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (lds_i32x2*)((const __attribute__((address_space(3))) char*)(addr)));
+          vf[dt][2 * qv] = x[0];
+          vf[dt][2 * qv + 1] = x[1];
+        }
       // ---- softmax (as the bf16 kernel)
       // Raw scores stay raw: masked pairs become -inf in place (the log2
       // multiplier is > 0) and the multiplier folds into the exponent's FMA,
@@ -277,24 +294,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int lo = pack_fp8<false>(st[t][r0], st[t][r0 + 1], 0);
         pb[w] = pack_fp8<true>(st[t][r0 + 2], st[t][r0 + 3], lo);
       }
-      // ---- O^T += V^T P^T: A-operand byte p of a lane is V[kappa(hh, p)][d]
+      // ---- O^T += V^T P^T
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        i32x8 vf;
-#pragma unroll
-        for (int qv = 0; qv < 4; ++qv) {
-          const int pk = 8 * qv + (L >> 1);                 // k-slot this lane addresses
-          const int key = 32 * (pk >> 4) + 8 * ((pk & 15) >> 2) + 4 * hh + (pk & 3);
-          const int ch = 2 * dt + g16;
-          const char* addr = vs + key * D + swz8<D>(key, ch) * 16 + 8 * (L & 1);
-          typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
-          const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (lds_i32x2*)((const __attribute__((address_space(3))) char*)(addr)));
-          vf[2 * qv] = x[0];
-          vf[2 * qv + 1] = x[1];
-        }
-        acc[dt] = mfma_fp8(vf, pb, acc[dt], svb, 127);
-      }
+      for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma_fp8(vf[dt], pb, acc[dt], svb, 127);
     }
     wait_loads();
     __syncthreads();
