@@ -325,7 +325,9 @@ int fa_fp8_quantize(const void* x, void* x8, uint8_t* scales, int rows, int S, i
  * product, while the row sum uses them unrounded.  scale multiplies the
  * dequantized q . k.  Masks: FA_MASK_NONE, FA_MASK_CAUSAL,
  * FA_MASK_SLIDING_WINDOW (FA_MASK_DOCUMENT -> FA_ERR_UNSUPPORTED); no score
- * modifier.  D in {64, 128}; tensors 16-byte aligned. */
+ * modifier.  Of mask_params only window is read (no visited counters, work
+ * queue or workgroup trace on this path).  D in {64, 128}; tensors 16-byte
+ * aligned. */
 int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const uint8_t* q_scale, const uint8_t* k_scale,
                const uint8_t* v_scale, void* out, float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int D,
                float scale, int mask_kind, const fa_mask_params* mask_params, void* stream);
