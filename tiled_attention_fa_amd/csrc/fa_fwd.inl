@@ -47,13 +47,16 @@ namespace miattn {
 //   relative bias: x = raw scale + T[h][i - j + Skv - 1] (natural units),
 //            mult = log2(e).
 // partial: 0 = no masking (full tile), 1 = the pair is admissible iff j < Skv
-// and j <= qi, 3 = iff also qi - j < window, 2 = admissible iff ok(j, jr)
-// (jr = c + 4hh).  bias(c):
+// and j <= qi, 3 = iff also qi - j < window, 2 = admissible iff ok(j, x),
+// x = aux(jr) the entry (document id) of the key at in-step offset
+// jr = c + 4hh; with GROUP4 aux4(jr0) gives the entries of four consecutive
+// keys jr0 .. jr0 + 3 at once (one 16-byte LDS read for four scores; off
+// where the registers for them would spill).  bias(c):
 // relative-bias entry of in-step key offset c + 4hh.  qw0: first row of the wave.
-template <int MOD, int NT, typename Ok, typename Bias>
+template <int MOD, int NT, bool GROUP4, typename Ok, typename Aux, typename Aux4, typename Bias>
 __device__ __forceinline__ float transform_scores(f32x16 (&st)[NT], int partial, int k0, int qi, int qw0, int hh,
-                                                  int Skv, float slope, const FwdArgs& a, Ok ok, Bias bias,
-                                                  float& mult) {
+                                                  int Skv, float slope, const FwdArgs& a, Ok ok, Aux aux,
+                                                  Aux4 aux4, Bias bias, float& mult) {
   const float c1 = a.scale_log2;
   float mb = kNegInf;
   bool plain = MOD == MOD_NONE;
@@ -97,9 +100,17 @@ __device__ __forceinline__ float transform_scores(f32x16 (&st)[NT], int partial,
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int jr = 32 * t + 8 * (r >> 2) + (r & 3) + 4 * hh;
-          st[t][r] = ok(k0 + jr, jr) ? st[t][r] : masked;
+        for (int q = 0; q < 4; ++q) {
+          const int jr0 = 32 * t + 8 * q + 4 * hh;
+          if constexpr (GROUP4) {
+            const i32x4 x = aux4(jr0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st[t][4 * q + e] = ok(k0 + jr0 + e, x[e]) ? st[t][4 * q + e] : masked;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              st[t][4 * q + e] = ok(k0 + jr0 + e, aux(jr0 + e)) ? st[t][4 * q + e] : masked;
+          }
         }
     }
   };
@@ -436,13 +447,11 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs& a, int P, uint64_t t0, i
         mode = mode ? 3 : 0;
       }
       float mult;
-      float mb = transform_scores<MOD, NT>(
+      float mb = transform_scores<MOD, NT, !(MASK == MASK_DOCUMENT && MOD == MOD_BOOST)>(
           st, mode, k0, qi, qw0, hh, Skv, slope, a,
-          [&](int j, int jr) {
-            int dj = 0;
-            if constexpr (MASK == MASK_DOCUMENT) dj = ds[jr];
-            return j < Skv && mask_ok<MASK>(qi, j, window, doc_i, dj);
-          },
+          [&](int j, int dj) { return j < Skv && mask_ok<MASK>(qi, j, window, doc_i, dj); },
+          [&](int jr) { return MASK == MASK_DOCUMENT ? ds[jr] : 0; },
+          [&](int jr0) { return MASK == MASK_DOCUMENT ? *(const i32x4*)(ds + jr0) : i32x4{0, 0, 0, 0}; },
           [&](int c) { return REL ? bl[CMAX - c] : 0.0f; }, mult);
       mb = half_swap_max(mb);
       const float m_new = fmaxf(m, mb);
@@ -771,11 +780,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // bl[59 - c] is the bias of key k0 + c + 4hh (c = 32t + 8(r/4) + r%4).
     const float* bl = bs + (qi - q0 + 4 - 4 * hh);
     float mult;
-    float mb = transform_scores<MOD, NT>(
+    float mb = transform_scores<MOD, NT, false>(
         st, cls_s == TILE_PARTIAL ? (MASK == MASK_CAUSAL ? 1 : MASK == MASK_WINDOW ? 3 : 2) : 0, k0, qi, qw0, hh,
         Skv, slope, a,
         [&](int j, int) { return j < Skv && mask_ok<MASK>(qi, j, window, 0, 0); },
-        [&](int c) { return REL ? bl[59 - c] : 0.0f; }, mult);
+        [](int) { return 0; }, [](int) { return i32x4{0, 0, 0, 0}; }, [&](int c) { return REL ? bl[59 - c] : 0.0f; },
+        mult);
     mb = half_swap_max(mb);
     const float m_new = fmaxf(m, mb);
     const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
