@@ -280,6 +280,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           const int ir = 8 * rq + hh4;
           const f32x4 L4 = *(const f32x4*)&ls[ir];
           const f32x4 E4 = *(const f32x4*)&es[ir];
+          // Document ids of the four query rows, one 16-byte read.
+          i32x4 D4 = {0, 0, 0, 0};
+          if constexpr (MASKED && MASK == MASK_DOCUMENT) D4 = *(const i32x4*)&dcs[ir];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = q0 + ir + e;
@@ -287,7 +290,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             recompute_p<MOD>(sp[4 * rq + e], i, kj, slope, REL ? bl[8 * rq + e] : 0.0f, a, L4[e], p, grad);
             if constexpr (MASKED) {
               int di = 0;
-              if constexpr (MASK == MASK_DOCUMENT) di = dcs[ir + e];
+              if constexpr (MASK == MASK_DOCUMENT) di = D4[e];
               const bool ok = col_ok && i < Sq && mask_ok<MASK>(i, kj, window, di, doc_j);
               p = ok ? p : 0.0f;
             }
@@ -585,21 +588,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         auto pds = [&](auto masked) {
           constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int c = 32 * t + 8 * (rr >> 2) + (rr & 3);
-            const int jr = c + 4 * hh;
-            const int j = k0 + jr;
-            float p, grad;
-            recompute_p<MOD>(st[rr], qi, j, slope, REL ? bl[59 - c] : 0.0f, a, lse2, p, grad);
-            if constexpr (MASKED) {
-              int dj = 0;
-              if constexpr (MASK == MASK_DOCUMENT) dj = dcs[jr];
-              const bool ok = j < Skv && mask_ok<MASK>(qi, j, window, doc_i, dj);
-              p = ok ? p : 0.0f;
-            }
-            dpt[rr] = p * (dpt[rr] - del) * grad;
-            if constexpr (REL) {
-              if (want_grad) __hip_atomic_fetch_add(gl + (59 - c), dpt[rr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          for (int g4 = 0; g4 < 4; ++g4) {
+            // Document ids of four consecutive keys, one 16-byte read.
+            i32x4 D4 = {0, 0, 0, 0};
+            if constexpr (MASKED && MASK == MASK_DOCUMENT) D4 = *(const i32x4*)&dcs[32 * t + 8 * g4 + 4 * hh];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int rr = 4 * g4 + e;
+              const int c = 32 * t + 8 * g4 + e;
+              const int jr = c + 4 * hh;
+              const int j = k0 + jr;
+              float p, grad;
+              recompute_p<MOD>(st[rr], qi, j, slope, REL ? bl[59 - c] : 0.0f, a, lse2, p, grad);
+              if constexpr (MASKED) {
+                int dj = 0;
+                if constexpr (MASK == MASK_DOCUMENT) dj = D4[e];
+                const bool ok = j < Skv && mask_ok<MASK>(qi, j, window, doc_i, dj);
+                p = ok ? p : 0.0f;
+              }
+              dpt[rr] = p * (dpt[rr] - del) * grad;
+              if constexpr (REL) {
+                if (want_grad)
+                  __hip_atomic_fetch_add(gl + (59 - c), dpt[rr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+              }
             }
           }
         };
