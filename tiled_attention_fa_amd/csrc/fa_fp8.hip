@@ -268,14 +268,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
       const float alpha = fast_exp2(m - m_use);
       const float mult = a.scale_log2;
-      float ps = 0.0f;
+      float ps = 0.0f;  // the first term starts the sum (no add of 0)
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = fast_exp2(__builtin_fmaf(st[t][r], mult, -m_use));
           st[t][r] = p;
-          ps += p;
+          ps = (t == 0 && r == 0) ? p : ps + p;
         }
       row_sum_update(l, lc, alpha, ps);
       m = m_new;
@@ -291,7 +291,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         const int t = w >> 2, r0 = 4 * (w & 3);
-        const int lo = pack_fp8<false>(st[t][r0], st[t][r0 + 1], 0);
+        // The first conversion writes the low half-word and the second the
+        // high one, so the first's other half may start as anything: a
+        // register an empty asm statement claims to define, rather than a
+        // zero moved into place.
+        int any;
+        asm volatile("" : "=v"(any));
+        const int lo = pack_fp8<false>(st[t][r0], st[t][r0 + 1], any);
         pb[w] = pack_fp8<true>(st[t][r0 + 2], st[t][r0 + 3], lo);
       }
       // ---- O^T += V^T P^T

@@ -458,14 +458,14 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs& a, int P, uint64_t t0, i
       const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
       const float alpha = fast_exp2(m - m_use);
       // ---- probabilities, row sum
-      float ps = 0.0f;
+      float ps = 0.0f;  // the first term starts the sum (no add of 0)
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = fast_exp2(__builtin_fmaf(st[t][r], mult, -m_use));
           st[t][r] = p;
-          ps += p;
+          ps = (t == 0 && r == 0) ? p : ps + p;
         }
       row_sum_update(l, lc, alpha, ps);
       m = m_new;
@@ -790,14 +790,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float m_new = fmaxf(m, mb);
     const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
     const float alpha = fast_exp2(m - m_use);
-    float ps = 0.0f;
+    float ps = 0.0f;  // the first term starts the sum (no add of 0)
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = fast_exp2(__builtin_fmaf(st[t][r], mult, -m_use));
         st[t][r] = p;
-        ps += p;
+        ps = (t == 0 && r == 0) ? p : ps + p;
       }
     row_sum_update(l, lc, alpha, ps);
     m = m_new;
