@@ -360,7 +360,11 @@ int fa_block_mask_build(int mask_kind, const fa_mask_params* mask_params,
 
 const char* fa_status_str(int status);
 
-/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH: FA_VERSION of the
+ * header it was built from.  0.2.0: fa_mask_params gained work_queue and
+ * wg_trace (a caller built against an older header passes a shorter
+ * struct, so check fa_version() == FA_VERSION first). */
+#define FA_VERSION 200
 int fa_version(void);
 
 #ifdef __cplusplus

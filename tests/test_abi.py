@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_host_helpers():
-    assert fa.fa_version() == 100
+    assert fa.fa_version() == binding.FA_VERSION
     assert fa.fa_status_str(0) == "ok"
     assert "workspace" in fa.fa_status_str(fa.FA_ERR_WORKSPACE)
     assert fa.fa_fwd_kv_step(128, fa.FA_BF16) == 64
@@ -93,6 +93,7 @@ def test_fwd_rejects_misaligned_wg_trace():
 
 def test_header_constants_match_binding():
     defines = dict(re.findall(r"^#define\s+(FA_\w+)\s+(.+)$", open(HEADER).read(), flags=re.M))
+    assert int(defines["FA_VERSION"]) == binding.FA_VERSION
     assert int(defines["FA_WORK_QUEUE_INTS"]) == fa.FA_WORK_QUEUE_INTS
     assert int(defines["FA_WG_TRACE_WORDS"]) == fa.FA_WG_TRACE_WORDS
     assert eval(defines["FA_NOALLOC_SCRATCH_BYTES"].replace("(size_t)", "")) == fa.FA_NOALLOC_SCRATCH_BYTES

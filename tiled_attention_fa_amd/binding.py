@@ -27,6 +27,7 @@ BLOCK = 128
 
 FA_BWD_DELTA, FA_BWD_DKDV, FA_BWD_DQ = 1, 2, 4
 
+FA_VERSION = 200  # the header's FA_VERSION: the struct layouts below
 EXPORTED = ("fa_fwd", "fa_fwd_kv_step", "fa_bwd", "fa_bwd_phase", "fa_bwd_noalloc", "fa_bwd_workspace_bytes",
             "fa_bwd_ds_workspace_bytes",
             "fa_bwd_rel_bias_workspace_bytes",
@@ -72,7 +73,11 @@ def lib() -> ctypes.CDLL:
     if _LIB is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m tiled_attention_fa_amd.build`")
-        _LIB = declare_prototypes(ctypes.CDLL(LIB_PATH))
+        L = declare_prototypes(ctypes.CDLL(LIB_PATH))
+        if L.fa_version() != FA_VERSION:
+            raise RuntimeError(f"{LIB_PATH} is version {L.fa_version()}, this binding needs {FA_VERSION} "
+                               "(the parameter structs differ): rebuild it with `python -m tiled_attention_fa_amd.build`")
+        _LIB = L
     return _LIB
 
 

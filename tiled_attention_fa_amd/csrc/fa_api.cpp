@@ -136,7 +136,7 @@ int check_tensor(const void* p, bool nonempty) {
 
 extern "C" {
 
-int fa_version(void) { return 100; }
+int fa_version(void) { return FA_VERSION; }
 
 const char* fa_status_str(int s) {
   switch (s) {
