@@ -231,14 +231,18 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const v
            int score_mod_kind, const fa_mod_params* mod_params,
            const fa_block_mask* block_mask, void* stream);
 
-/* The three launches of fa_bwd, one at a time: FA_BWD_DELTA writes
- * rowsum(dout * out) into the workspace; FA_BWD_DKDV writes dk and dv;
- * FA_BWD_DQ writes dq.  Same arguments and validation as fa_bwd.  With a
- * workspace of fa_bwd_workspace_bytes, DKDV and DQ only read what DELTA
- * wrote, so once DELTA has finished they may run concurrently on different
- * streams; with the stored-dS workspace (fa_bwd_ds_workspace_bytes) DQ reads
- * what DKDV wrote and must follow it.  Calling the three in order on one
- * stream is exactly fa_bwd. */
+/* The phases of fa_bwd, any subset per call (a bit mask): FA_BWD_DELTA
+ * writes rowsum(dout * out) and the LSE in log2 units into the workspace;
+ * FA_BWD_DKDV writes dk and dv; FA_BWD_DQ writes dq.  Same arguments and
+ * validation as fa_bwd.  With a workspace of fa_bwd_workspace_bytes, DKDV
+ * and DQ only read what DELTA wrote, so once DELTA has finished they may run
+ * concurrently on different streams; with the stored-dS workspace
+ * (fa_bwd_ds_workspace_bytes) DQ reads what DKDV wrote and must follow it.
+ * A call holding both DELTA and DQ (without stored dS) runs them as one
+ * launch, the dQ kernel computing the row sums of its own rows, then DKDV if
+ * asked; fa_bwd is that call with all three.  Every split of the phases over
+ * calls in the order DELTA, DKDV, DQ (or DELTA + DQ, then DKDV) on one stream
+ * gives the same bits as fa_bwd. */
 enum { FA_BWD_DELTA = 1, FA_BWD_DKDV = 2, FA_BWD_DQ = 4 };
 int fa_bwd_phase(int phase, const void* q, const void* k, const void* v, const void* out,
                  const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,

@@ -192,6 +192,62 @@ def test_phases_on_two_streams():
         assert torch.equal(got, want), what
 
 
+FUSED_CASES = [
+    # (B, Hq, Hkv, Sq, Skv, D, spec, block mask)
+    (1, 4, 2, 333, 333, 64, dict(mask=fa.MASK_CAUSAL), False),
+    (2, 4, 4, 700, 700, 128, dict(mask=fa.MASK_NONE, mod=fa.MOD_SOFTCAP, softcap=30.0), False),
+    (1, 4, 2, 333, 500, 128, dict(mask=fa.MASK_CAUSAL, mod=fa.MOD_ALIBI), False),
+    (2, 2, 1, 900, 900, 128, dict(mask=fa.MASK_DOCUMENT), True),
+    (1, 2, 2, 450, 450, 64, dict(mask=fa.MASK_SLIDING_WINDOW, window=100, mod=fa.MOD_LOCAL_BOOST, boost_radius=40,
+                                boost_factor=1.1), True),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[f"D{c[5]}-S{c[3]}x{c[4]}-m{c[6]['mask']}-bm{int(c[7])}"
+                                                   for c in FUSED_CASES])
+def test_fused_row_pass_same_bits(case):
+    """A call holding DELTA and DQ runs one launch, the dQ kernel doing the
+    row pass for its own rows.  Its row arrays (rowsum(dO * O), LSE in log2
+    units) and all three gradients must equal, bit for bit, those of the row
+    pass and the kernels launched one by one, for every split of the phases."""
+    B, Hq, Hkv, Sq, Skv, D, spec, use_bm = case
+    q, _, _ = synth.qkv(B, Hq, Hkv, Sq, Sq, D, 80 + Sq)
+    _, k, v = synth.qkv(B, Hq, Hkv, Skv, Skv, D, 81 + Skv)
+    q, k, v = dev(q), dev(k), dev(v)
+    do = dev(synth.randn((B, Hq, Sq, D), 82))
+    doc = dev(doc_ids_for(B, Sq, 83)) if spec["mask"] == fa.MASK_DOCUMENT else None
+    bm = None
+    if use_bm:
+        bm = fa.build_block_mask(spec["mask"], B, Sq, Skv, window=spec.get("window", 0), doc_ids=doc)
+    kw = dict(doc_ids=doc, block_mask=bm, **spec)
+    o, lse = fa.forward(q, k, v, return_lse=True, **kw)
+    ws_bytes = fa.fa_bwd_workspace_bytes(B, Hq, Sq, D)
+
+    def run(splits):
+        ws = torch.full((ws_bytes,), 0xFF, dtype=torch.uint8, device="cuda")
+        grads = tuple(torch.full_like(t, float("nan")) for t in (q, k, v))
+        for ph in splits:
+            fa.backward(q, k, v, o, do, lse, workspace=ws, grads=grads, phases=ph, **kw)
+        torch.cuda.synchronize()
+        return ws, grads
+
+    one_by_one = run([fa.FA_BWD_DELTA, fa.FA_BWD_DKDV, fa.FA_BWD_DQ])
+    rows_then_kv = run([fa.FA_BWD_DELTA | fa.FA_BWD_DQ, fa.FA_BWD_DKDV])
+    all_in_one = run([fa.FA_BWD_DELTA | fa.FA_BWD_DKDV | fa.FA_BWD_DQ])
+    n = B * Hq * Sq
+    half = (n * 4 + 255) // 256 * 256
+    ref_rows = [one_by_one[0][:n * 4].view(torch.float32), one_by_one[0][half:half + n * 4].view(torch.float32)]
+    for got, label in ((rows_then_kv, "DELTA|DQ, DKDV"), (all_in_one, "fa_bwd")):
+        assert torch.equal(got[0][:n * 4], one_by_one[0][:n * 4]), (label, "rowsum(dO * O)")
+        assert torch.equal(got[0][half:half + n * 4], one_by_one[0][half:half + n * 4]), (label, "LSE log2")
+        for g, r, what in zip(got[1], one_by_one[1], ("dQ", "dK", "dV")):
+            assert torch.equal(g, r), (label, what)
+    # The row pass itself against its definition on the rounded O (fp64 here).
+    want = (do.double() * o.double()).sum(-1).reshape(-1)
+    assert torch.allclose(ref_rows[0].double(), want, rtol=1e-5, atol=1e-5)
+    assert not torch.isnan(ref_rows[1]).any()
+
+
 @pytest.mark.parametrize("B,Hq,Hkv,S", [(2, 8, 4, 700), (4, 8, 2, 200)])
 def test_xcd_pinned_schedule(B, Hq, Hkv, S):
     """dQ and dK/dV under the XCD-pinned schedule (B * Hkv a multiple of 8),

@@ -112,6 +112,10 @@ struct BwdArgs {
   // Debug records (fa_mask_params.wg_trace): the dK/dV workgroups' first,
   // then the dQ workgroups' from record B * Hkv * n_kt on.
   int64_t* trace;
+  // Set by the launcher, not the caller: the dQ kernel computes delta and
+  // lse2 of its own rows and writes them for the dK/dV kernel that follows
+  // (no separate row pass).
+  int fuse_rows;
 };
 
 // Elements of one stored dS block: 4 waves x 64 lanes x 16 bf16.

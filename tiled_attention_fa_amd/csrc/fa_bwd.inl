@@ -23,6 +23,20 @@ namespace miattn {
 // ---------------------------------------------------------------- row pass
 // delta[row] = rowsum(dO * O); lse2[row] = LSE * log2(e), or +inf for rows
 // with no admissible key (their probabilities are all zero).
+//
+// A row's delta is the sum of D / 8 partials over 16-byte chunks (dot8_bf16,
+// chunk c = elements 8c .. 8c + 7), combined as a halving tree: partial c
+// with partial c + D / 16, then c with c + D / 32, ... down to chunks 0 and 1.
+// Both the row pass below and the dQ kernel's fused row pass (fuse_rows)
+// follow exactly this order, so they give the same bits.
+__device__ __forceinline__ float dot8_bf16(const u32x4& x, const u32x4& y) {
+  float s = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s += bf16_lo(x[e]) * bf16_lo(y[e]) + bf16_hi(x[e]) * bf16_hi(y[e]);
+  return s;
+}
+__device__ __forceinline__ float lse_log2(float L) { return (L == kNegInf) ? __builtin_inff() : L * kLog2e; }
+
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restrict__ o,
                                                         const uint16_t* __restrict__ dout,
@@ -32,18 +46,13 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
   const long row = (long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
   const int c = threadIdx.x % LPR;
   float s = 0.0f;
-  if (row < rows) {
-    const u32x4 x = *(const u32x4*)(o + row * D + c * 8);
-    const u32x4 y = *(const u32x4*)(dout + row * D + c * 8);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s += bf16_lo(x[e]) * bf16_lo(y[e]) + bf16_hi(x[e]) * bf16_hi(y[e]);
-  }
+  if (row < rows) s = dot8_bf16(*(const u32x4*)(o + row * D + c * 8), *(const u32x4*)(dout + row * D + c * 8));
+  // Lane c adds lane c ^ w: the halving tree (addition is commutative).
 #pragma unroll
   for (int w = LPR / 2; w >= 1; w >>= 1) s += __shfl_xor(s, w, LPR);
   if (row < rows && c == 0) {
     delta[row] = s;
-    const float L = lse[row];
-    lse2[row] = (L == kNegInf) ? __builtin_inff() : L * kLog2e;
+    lse2[row] = lse_log2(lse[row]);
   }
 }
 
@@ -427,8 +436,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     qf[c] = row_ok ? ((const u32x4*)Qrow)[2 * c + hh] : u32x4{0, 0, 0, 0};
     of[c] = row_ok ? ((const u32x4*)dOrow)[2 * c + hh] : u32x4{0, 0, 0, 0};
   }
-  const float lse2 = row_ok ? a.lse2[ri] : __builtin_inff();
-  const float del = row_ok ? a.delta[ri] : 0.0f;
+  float lse2, del;
+  if (a.fuse_rows) {
+    // The row pass for this lane's row: this lane holds chunks 2c + hh of
+    // dO (c < KC), the other half-wave the rest.  The halving tree over the
+    // chunk index pairs chunk 2c + hh with 2(c + w) + hh for w = KC/2 .. 1
+    // in-lane, then the two half-waves.
+    const uint16_t* Orow = (const uint16_t*)a.o + ri * D;
+    float part[KC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      part[c] = dot8_bf16(row_ok ? ((const u32x4*)Orow)[2 * c + hh] : u32x4{0, 0, 0, 0}, of[c]);
+#pragma unroll
+    for (int w = KC / 2; w >= 1; w >>= 1)
+#pragma unroll
+      for (int c = 0; c < w; ++c) part[c] += part[c + w];
+    del = half_swap_sum(part[0]);
+    lse2 = row_ok ? lse_log2(a.lse[ri]) : __builtin_inff();
+    if (row_ok && hh == 0) {
+      a.delta[ri] = del;
+      const_cast<float*>(a.lse2)[ri] = lse2;
+    }
+  } else {
+    lse2 = row_ok ? a.lse2[ri] : __builtin_inff();
+    del = row_ok ? a.delta[ri] : 0.0f;
+  }
   const uint16_t* K = (const uint16_t*)a.k + (size_t)(b * a.Hkv + hk) * Skv * D;
   const uint16_t* V = (const uint16_t*)a.v + (size_t)(b * a.Hkv + hk) * Skv * D;
   const int32_t* doc = nullptr;
@@ -834,9 +866,26 @@ __global__ __launch_bounds__(256) void bias_grad_reduce_kernel(const float* __re
 }
 
 template <int D, int MASK, int MOD, bool BM>
-static hipError_t launch_bwd_mm(const BwdArgs& a, int phases, hipStream_t st) {
+static hipError_t launch_bwd_mm(const BwdArgs& a_in, int phases, hipStream_t st) {
+  BwdArgs a = a_in;
   const long rows = (long)a.B * a.Hq * a.Sq;
   const int rows_per_block = 256 / (D / 8);
+  // Stored dS (the host sets a.ds only for these variants): the dK/dV kernel
+  // writes dS and the dQ kernel reads it.
+  constexpr bool DS_OK = (MASK == MASK_NONE || MASK == MASK_CAUSAL) && !BM && MOD != MOD_REL_BIAS;
+  const bool use_ds = DS_OK && a.ds != nullptr;
+  // The row pass and the recomputing dQ kernel in one call: one launch, the
+  // dQ kernel doing the row pass for its own rows (and writing them for a
+  // dK/dV launch that follows).  Same bits as the two launches.
+  const int asked = phases;
+  if ((phases & 5) == 5 && !use_ds && rows > 0) {
+    a.fuse_rows = 1;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, MASK, MOD, BM>), dim3((unsigned)(a.B * a.Hq * a.n_qt)), dim3(256), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.fuse_rows = 0;
+    phases &= ~5;
+  }
   if ((phases & 1) && rows > 0) {
     hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
                        dim3(256), 0, st, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, a.delta,
@@ -844,10 +893,6 @@ static hipError_t launch_bwd_mm(const BwdArgs& a, int phases, hipStream_t st) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // Stored dS (the host sets a.ds only for these variants): the dK/dV kernel
-  // writes dS and the dQ kernel reads it.
-  constexpr bool DS_OK = (MASK == MASK_NONE || MASK == MASK_CAUSAL) && !BM && MOD != MOD_REL_BIAS;
-  const bool use_ds = DS_OK && a.ds != nullptr;
   // dK, dV are written for every key (zero when no query sees it).
   if ((phases & 2) && (long)a.B * a.Hkv * a.n_kt > 0) {
     const dim3 grid((unsigned)(a.B * a.Hkv * a.n_kt));
@@ -880,7 +925,7 @@ static hipError_t launch_bwd_mm(const BwdArgs& a, int phases, hipStream_t st) {
   if constexpr (MOD == MOD_REL_BIAS) {
     // The table gradient (also when there are no rows: then it is zero).
     const int tlen = a.Sq + a.Skv - 1;
-    if ((phases & 4) && a.mod.rel_bias_grad != nullptr && tlen > 0) {
+    if ((asked & 4) && a.mod.rel_bias_grad != nullptr && tlen > 0) {
       const int per_head = (tlen + 255) / 256;
       hipLaunchKernelGGL((bias_grad_reduce_kernel<D>), dim3((unsigned)(a.Hq * per_head)), dim3(256), 0, st,
                          a.mod.rel_bias_part, a.mod.rel_bias_grad, rows > 0 ? a.B : 0, a.Hq, a.n_qt, a.Skv, tlen,

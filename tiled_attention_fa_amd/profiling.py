@@ -424,12 +424,15 @@ def write_bench_table(which: str, out: str) -> str:
                   "(the first shown):", "", "```", cmd, "```", "",
                   "TFLOP/s count admissible pairs only (4 D forward, 10 D backward). Kernel times are HIP-event "
                   f"averages over {BENCH_STEPS} steps after {BENCH_WARMUP} warm-up steps.", "",
+                  "dQ ms includes the row pass (rowsum(dO * O)) fused into the dQ kernel; a separate row-pass "
+                  "launch, where a run has one, is listed as delta ms.", "",
                   "| S | B | fwd+bwd TFLOP/s | fwd TFLOP/s | bwd TFLOP/s | fwd ms | delta ms | dK/dV ms | dQ ms |",
                   "|---|---|---|---|---|---|---|---|---|"]
         for lab, _, r in recs:
             c, k = r["config"], r["kernel_ms"]
+            delta = f"{k['bwd_delta']:.3f}" if "bwd_delta" in k else "-"
             lines.append(f"| {c['S']} | {c['B']} | {r['value']:.1f} | {r['fwd_tflops']:.1f} | {r['bwd_tflops']:.1f} | "
-                         f"{k['fwd']:.3f} | {k['bwd_delta']:.3f} | {k['bwd_dkdv']:.3f} | {k['bwd_dq']:.3f} |")
+                         f"{k['fwd']:.3f} | {delta} | {k['bwd_dkdv']:.3f} | {k['bwd_dq']:.3f} |")
         name = "causal_by_seqlen.md"
     else:
         lines += ["# Schedule and dQ variants, one MI355X", "",
