@@ -450,8 +450,8 @@ def backward(q, k, v, out, dout, lse, *, scale=None, mask=MASK_NONE, window=0, d
              phases=FA_BWD_DELTA | FA_BWD_DKDV | FA_BWD_DQ, noalloc=False, store_ds=False, wg_trace=None):
     """(dq, dk, dv) of sum(O * dout), recomputing P from ``lse``.
 
-    ``phases`` selects which of the three backward launches run (all by
-    default, which is fa_bwd).  ``noalloc``: call fa_bwd_noalloc, whose
+    ``phases`` selects which backward phases run (all by default, which is
+    fa_bwd; the row pass and dQ in one call share one launch).  ``noalloc``: call fa_bwd_noalloc, whose
     workspace is the library's fixed device scratch (all phases; with
     ``grads`` given and no relative-bias gradient nothing is allocated).
     ``store_ds``: allocate the stored-dS workspace (fa_bwd_ds_workspace_bytes)

@@ -7,11 +7,12 @@
 //   P = exp(mod(scale q.k) - LSE), dV = P^T dO, dP = dO V^T,
 //   delta_i = rowsum(dO_i * O_i), dS = P (dP - delta) mod',
 //   dQ = scale dS K, dK = scale dS^T Q.
-// Three launches on one stream: the row pass (delta and LSE in log2 units),
-// then a key-stationary kernel that owns 128 keys and loops over every query
-// head of its GQA group and every query step (dK, dV accumulated in
-// registers, written once), then a query-stationary kernel for dQ (like the
-// forward pass).  Nothing is accumulated with atomics, so the results are
+// Three phases on one stream: the row pass (delta and LSE in log2 units), a
+// key-stationary kernel that owns 128 keys and loops over every query head of
+// its GQA group and every query step (dK, dV accumulated in registers,
+// written once), and a query-stationary kernel for dQ (like the forward
+// pass).  When one call asks for the row pass and dQ, the dQ kernel does the
+// row pass for its own rows and runs first (two launches instead of three).  Nothing is accumulated with atomics, so the results are
 // deterministic.  Q/dO (resp. K/V) tiles go straight from memory into
 // per-stage LDS objects, with the step loop unrolled by two.
 #include <type_traits>
