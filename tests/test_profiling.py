@@ -170,3 +170,40 @@ def test_wgtrace_decode_and_stats(tmp_path, monkeypatch):
     monkeypatch.setattr(profiling, "PROFILES", str(tmp_path / "profiles"))
     text = open(profiling.write_wgtrace_summary("gqa_causal", str(tmp_path / "out"))).read()
     assert "--wg-trace" in text and "| 0 | 3 |" in text
+
+
+def test_stall_stats_and_summary(tmp_path, monkeypatch):
+    """The stall passes' counters as fractions: wave-time counters over
+    SQ_WAVE_CYCLES, matrix-core counters over cycles x SIMDs, LDS counters
+    over cycles x compute units; warm-up dispatches left out."""
+    out = tmp_path / "out"
+    w = out / "gqa_causal"
+    n = profiling.BENCH_WARMUP + profiling.BENCH_STEPS
+    cyc = 1.5e5  # per dispatch; SQ_BUSY_CYCLES is summed over the shader engines
+    a = {"SQ_WAVE_CYCLES": 1000.0, "SQ_WAIT_ANY": 400.0, "SQ_WAIT_INST_ANY": 250.0, "SQ_WAIT_INST_LDS": 50.0,
+         "SQ_ACTIVE_INST_ANY": 600.0, "SQ_ACTIVE_INST_VALU": 300.0, "SQ_ACTIVE_INST_LDS": 100.0,
+         "SQ_BUSY_CYCLES": cyc * profiling.SHADER_ENGINES}
+    b = {"SQ_VALU_MFMA_BUSY_CYCLES": 0.6 * cyc * profiling.SIMDS, "SQ_VALU_MFMA_COEXEC_CYCLES": 0.15 * cyc * profiling.SIMDS,
+         "SQ_LDS_IDX_ACTIVE": 0.5 * cyc * profiling.COMPUTE_UNITS, "SQ_LDS_DATA_FIFO_FULL": 0.0,
+         "SQ_LDS_CMD_FIFO_FULL": 0.01 * cyc * profiling.COMPUTE_UNITS,
+         "SQ_INSTS_LDS_LOAD_BANDWIDTH": 2.0 * cyc * profiling.COMPUTE_UNITS, "SQ_INSTS_MFMA": 128.0 * cyc,
+         "SQ_BUSY_CYCLES": cyc * profiling.SHADER_ENGINES}
+    assert set(a) == set(profiling.STALL_PASSES["stallA"]) and set(b) == set(profiling.STALL_PASSES["stallB"])
+    for name, ctrs in (("stallA", a), ("stallB", b)):
+        rows = []
+        for d in range(1, n + 1):
+            warm = d <= profiling.BENCH_WARMUP
+            # every counter split over two rows; warm-up dispatches read 3x
+            rows += [(d, FWD, c, (3.0 if warm else 1.0) * v / 2) for c, v in ctrs.items() for _ in range(2)]
+        _counters(w / name, rows)
+    st = profiling.stall_stats("gqa_causal", str(out))["fwd"]
+    assert st["wait_dependency"] == pytest.approx(0.4) and st["wait_issue"] == pytest.approx(0.25)
+    assert st["wait_issue_lds"] == pytest.approx(0.05) and st["active_any"] == pytest.approx(0.6)
+    assert st["active_valu"] == pytest.approx(0.3) and st["active_lds"] == pytest.approx(0.1)
+    assert st["mfma_busy"] == pytest.approx(0.6) and st["mfma_coexec"] == pytest.approx(0.25)
+    assert st["lds_active"] == pytest.approx(0.5) and st["lds_cmd_fifo_full"] == pytest.approx(0.01)
+    assert st["lds_bytes_per_cu_cycle"] == pytest.approx(128.0)
+    assert st["lds_bytes_per_mfma"] == pytest.approx(64.0 * 2.0 * profiling.COMPUTE_UNITS / 128.0)
+    monkeypatch.setattr(profiling, "PROFILES", str(tmp_path / "profiles"))
+    text = open(profiling.write_stall_summary("gqa_causal", str(out))).read()
+    assert "| fwd | 0.40 | 0.25 | 0.05 |" in text and "--pmc SQ_WAVE_CYCLES" in text

@@ -32,6 +32,13 @@ instruction mix and shader clock, summarised into profiles/.
         schedule, recomputed against stored dS for dQ, each twice, in
         alternation: schedule_and_dq_variants.md).
 
+    python -m tiled_attention_fa_amd.profiling stalls --workload W --out DIR
+    python -m tiled_attention_fa_amd.profiling stalls-summary --workload W --out DIR
+        Two more --pmc passes over the same bench.py run (STALL_PASSES): where
+        the waves spend their time (waiting for a dependency, waiting to
+        issue, issuing VALU or LDS instructions) and how busy the matrix
+        cores and the LDS are; then profiles/W_stalls.md, per kernel.
+
     python -m tiled_attention_fa_amd.profiling wgtrace --workload W --out DIR
     python -m tiled_attention_fa_amd.profiling wgtrace-summary --workload W --out DIR
         bench.py --wg-trace (no profiler): after the timed steps, one more
@@ -67,6 +74,15 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 SQ_COUNTERS = ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT",
                "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_SALU"]
+# Wave-time and LDS/matrix-core counters, 8 SQ counters per pass (the most
+# one pass can hold); SQ_BUSY_CYCLES in both gives each dispatch's cycles.
+STALL_PASSES = {
+    "stallA": ["SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_ANY",
+               "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_BUSY_CYCLES"],
+    "stallB": ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_DATA_FIFO_FULL",
+               "SQ_LDS_CMD_FIFO_FULL", "SQ_INSTS_LDS_LOAD_BANDWIDTH", "SQ_INSTS_MFMA", "SQ_BUSY_CYCLES"],
+}
+COMPUTE_UNITS = 256
 SHADER_ENGINES = 32
 SIMDS = 1024
 COPY_MIB = 1024
@@ -126,6 +142,14 @@ def passes(workload: str, out: str, shape=(0, 0)) -> list[tuple[str, list[str]]]
     return res
 
 
+def stall_passes(workload: str, out: str, shape=(0, 0)) -> list[tuple[str, list[str]]]:
+    wdir = os.path.join(out, label(workload, shape))
+    fmt = ["--output-format", "csv", "-o", "run"]
+    args = _bench_args(workload, BENCH_STEPS, BENCH_WARMUP, shape)
+    return [(name, ["rocprofv3", "--pmc", *ctrs, *fmt, "-d", os.path.join(wdir, name), "--", *args])
+            for name, ctrs in STALL_PASSES.items()]
+
+
 def calibration_passes(out: str) -> list[tuple[str, list[str]]]:
     fmt = ["--output-format", "csv", "-o", "run"]
     return [(f"copy_{c}", ["rocprofv3", "--pmc", c, *fmt, "-d", os.path.join(out, f"copy_{c}"), "--",
@@ -133,13 +157,16 @@ def calibration_passes(out: str) -> list[tuple[str, list[str]]]:
             for c in ("FETCH_SIZE", "WRITE_SIZE")]
 
 
-def run(workload: str, out: str, limit: int, shape=(0, 0)) -> None:
+def run(workload: str, out: str, limit: int, shape=(0, 0), stalls: bool = False) -> None:
     out = os.path.abspath(out)
     os.makedirs(out, exist_ok=True)
-    todo = passes(workload, out, shape)
     name_of = label(workload, shape)
-    if not os.path.isdir(os.path.join(out, "copy_WRITE_SIZE")):
-        todo = calibration_passes(out) + todo
+    if stalls:
+        todo = stall_passes(workload, out, shape)
+    else:
+        todo = passes(workload, out, shape)
+        if not os.path.isdir(os.path.join(out, "copy_WRITE_SIZE")):
+            todo = calibration_passes(out) + todo
     env = dict(os.environ, TMPDIR="/tmp")
     for name, argv in todo:
         print(f"profiling: {name_of} {name}", flush=True)
@@ -585,9 +612,87 @@ def write_wgtrace_summary(workload: str, out: str, shape=(0, 0)) -> str:
     return path
 
 
+def stall_stats(workload: str, out: str, shape=(0, 0)) -> dict[str, dict[str, float]]:
+    """Per bench.py timing key: the stall passes' counters over the timed
+    dispatches, as fractions.  The wave-time counters (SQ_WAVE_CYCLES,
+    SQ_WAIT_*, SQ_ACTIVE_INST_*) are summed over all waves in one unit, so
+    each is taken as a fraction of SQ_WAVE_CYCLES; the matrix-core counters
+    are per SIMD and the LDS ones per compute unit, taken over the
+    dispatch's cycles (SQ_BUSY_CYCLES / shader engines) times the SIMDs or
+    compute units."""
+    wdir = os.path.join(out, label(workload, shape))
+    a = _dispatch_sums(os.path.join(wdir, "stallA"))
+    b = _dispatch_sums(os.path.join(wdir, "stallB"))
+    res = {}
+    for name in a:
+        key = kernel_key(name)
+        if key is None or name not in b:
+            continue
+        x, y = a[name], b[name]
+        wave = x["SQ_WAVE_CYCLES"]
+        cyc_b = y["SQ_BUSY_CYCLES"] / SHADER_ENGINES
+        res[key] = {
+            "kernel_name": name,
+            "wait_dependency": x["SQ_WAIT_ANY"] / wave,
+            "wait_issue": x["SQ_WAIT_INST_ANY"] / wave,
+            "wait_issue_lds": x["SQ_WAIT_INST_LDS"] / wave,
+            "active_any": x["SQ_ACTIVE_INST_ANY"] / wave,
+            "active_valu": x["SQ_ACTIVE_INST_VALU"] / wave,
+            "active_lds": x["SQ_ACTIVE_INST_LDS"] / wave,
+            "mfma_busy": y["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc_b * SIMDS),
+            "mfma_coexec": y["SQ_VALU_MFMA_COEXEC_CYCLES"] / y["SQ_VALU_MFMA_BUSY_CYCLES"]
+            if y["SQ_VALU_MFMA_BUSY_CYCLES"] else 0.0,
+            "lds_active": y["SQ_LDS_IDX_ACTIVE"] / (cyc_b * COMPUTE_UNITS),
+            "lds_cmd_fifo_full": y["SQ_LDS_CMD_FIFO_FULL"] / (cyc_b * COMPUTE_UNITS),
+            "lds_data_fifo_full": y["SQ_LDS_DATA_FIFO_FULL"] / (cyc_b * COMPUTE_UNITS),
+            "lds_bytes_per_cu_cycle": 64.0 * y["SQ_INSTS_LDS_LOAD_BANDWIDTH"] / (cyc_b * COMPUTE_UNITS),
+            "lds_bytes_per_mfma": 64.0 * y["SQ_INSTS_LDS_LOAD_BANDWIDTH"] / y["SQ_INSTS_MFMA"]
+            if y.get("SQ_INSTS_MFMA") else 0.0,
+        }
+    return res
+
+
+def write_stall_summary(workload: str, out: str, shape=(0, 0)) -> str:
+    st = stall_stats(workload, out, shape)
+    lab = label(workload, shape)
+    extra = "".join(f" --{k} {v}" for k, v in (("batch", shape[0]), ("seq-len", shape[1])) if v)
+    lines = [f"# Where the waves spend their time: {lab}", "",
+             "Commands (repository root on the GPU host; rocprofv3 from /tmp, one counter pass each):", "", "```"]
+    for name, ctrs in STALL_PASSES.items():
+        lines.append(f"rocprofv3 --pmc {' '.join(ctrs)} --output-format csv -o run -d <out>/{lab}/{name} -- "
+                     f"python3 <repo>/bench.py --workload {workload} --no-cpu-baseline --steps {BENCH_STEPS} "
+                     f"--warmup {BENCH_WARMUP}{extra}")
+    lines += ["```", "",
+              f"Averages over the {BENCH_STEPS} timed dispatches of each kernel. Wave time (fractions of "
+              "SQ_WAVE_CYCLES, summed over all waves; the categories overlap): waiting on a dependency "
+              "(SQ_WAIT_ANY), waiting to issue (SQ_WAIT_INST_ANY; of it, LDS instructions: SQ_WAIT_INST_LDS), "
+              "working on any, VALU and LDS instructions (SQ_ACTIVE_INST_*). Matrix cores: SQ_VALU_MFMA_BUSY_CYCLES "
+              f"over the dispatch's cycles x {SIMDS} SIMDs, and the share of those cycles in which a VALU "
+              "instruction also issued (SQ_VALU_MFMA_COEXEC_CYCLES). LDS: SQ_LDS_IDX_ACTIVE and the FIFO-full "
+              f"counters over cycles x {COMPUTE_UNITS} compute units, loaded bytes (64 x "
+              "SQ_INSTS_LDS_LOAD_BANDWIDTH) per compute unit and cycle and per MFMA.", "",
+              "| kernel | wait dependency | wait issue | of it LDS | active any | active VALU | active LDS | MFMA busy "
+              "| MFMA co-exec VALU | LDS active | LDS cmd FIFO full | LDS data FIFO full | LDS B / CU cycle "
+              "| LDS B / MFMA |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for key, v in sorted(st.items()):
+        lines.append(f"| {key} | {v['wait_dependency']:.2f} | {v['wait_issue']:.2f} | {v['wait_issue_lds']:.2f} | "
+                     f"{v['active_any']:.2f} | {v['active_valu']:.2f} | {v['active_lds']:.2f} | {v['mfma_busy']:.2f} | "
+                     f"{v['mfma_coexec']:.2f} | {v['lds_active']:.2f} | {v['lds_cmd_fifo_full']:.3f} | "
+                     f"{v['lds_data_fifo_full']:.3f} | {v['lds_bytes_per_cu_cycle']:.1f} | "
+                     f"{v['lds_bytes_per_mfma']:.0f} |")
+    lines += ["", f"Kernel sources of these figures: hash `{source_sha()}`.", ""]
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, f"{lab}_stalls.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    return path
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("action", choices=["run", "summarize", "bench", "bench-summary", "wgtrace", "wgtrace-summary"])
+    ap.add_argument("action", choices=["run", "summarize", "bench", "bench-summary", "wgtrace", "wgtrace-summary",
+                                       "stalls", "stalls-summary"])
     ap.add_argument("--workload")
     ap.add_argument("--set", choices=["workloads", "seqlen", "variants"])
     ap.add_argument("--out", required=True)
@@ -611,6 +716,12 @@ def main() -> None:
         return
     if args.action == "wgtrace-summary":
         print(write_wgtrace_summary(args.workload, args.out, shape))
+        return
+    if args.action == "stalls":
+        run(args.workload, args.out, args.limit, shape, stalls=True)
+        return
+    if args.action == "stalls-summary":
+        print(write_stall_summary(args.workload, args.out, shape))
         return
     if args.action == "run":
         run(args.workload, args.out, args.limit, shape)
