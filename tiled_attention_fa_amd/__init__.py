@@ -14,7 +14,7 @@ from .binding import (  # noqa: F401
     lib, fa_fwd, fa_bwd, fa_bwd_phase, fa_bwd_noalloc, fa_block_mask_build, fa_bwd_workspace_bytes,
     fa_bwd_ds_workspace_bytes,
     fa_bwd_rel_bias_workspace_bytes, fa_block_mask_bytes, fa_fwd_kv_step,
-    fa_status_str, fa_version, default_scale, build_block_mask, forward, backward,
+    fa_status_str, fa_version, default_scale, build_block_mask, forward, backward, attention,
     FP8_BLOCK, quantize_fp8, forward_fp8, FA_WORK_QUEUE_INTS, new_work_queue,
     FA_WG_TRACE_WORDS, new_wg_trace, decode_wg_trace,
 )

@@ -513,3 +513,46 @@ def backward(q, k, v, out, dout, lse, *, scale=None, mask=MASK_NONE, window=0, d
     if want_bias_grad:
         return dq, dk, dv, rel_bias_grad
     return dq, dk, dv
+
+
+_ATTENTION_FN = None
+
+
+def _attention_fn():
+    """The torch.autograd.Function behind attention(), made on first use
+    (the binding imports torch lazily)."""
+    global _ATTENTION_FN
+    if _ATTENTION_FN is None:
+        torch = _torch()
+
+        class _Attention(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, rel_bias, opts):
+                o, lse = forward(q, k, v, rel_bias=rel_bias, return_lse=True, **opts)
+                ctx.save_for_backward(q, k, v, o, lse, rel_bias)
+                ctx.opts = opts
+                return o
+
+            @staticmethod
+            def backward(ctx, dout):
+                q, k, v, o, lse, rel_bias = ctx.saved_tensors
+                want_bias = rel_bias is not None and ctx.needs_input_grad[3]
+                res = backward(q, k, v, o, dout.contiguous(), lse, rel_bias=rel_bias,
+                               rel_bias_grad=True if want_bias else None, **ctx.opts)
+                return res[0], res[1], res[2], (res[3] if want_bias else None), None
+
+        _ATTENTION_FN = _Attention
+    return _ATTENTION_FN
+
+
+def attention(q, k, v, *, scale=None, mask=MASK_NONE, window=0, doc_ids=None, mod=MOD_NONE, alibi_slopes=None,
+              softcap=0.0, boost_radius=0, boost_factor=1.0, rel_bias=None, block_mask=None):
+    """O = softmax(mod(scale q k^T) masked) v as a differentiable torch
+    operation: fa_fwd (keeping its LSE) in the forward, fa_bwd in the backward,
+    giving dq, dk, dv (dk, dv summed over each GQA group) and, with MOD_REL_BIAS
+    and a ``rel_bias`` that requires grad, the bias table's gradient.  The other
+    arguments are those of forward() and carry no gradient.  The backward takes
+    bf16 inputs, like fa_bwd."""
+    opts = dict(scale=scale, mask=mask, window=window, doc_ids=doc_ids, mod=mod, alibi_slopes=alibi_slopes,
+                softcap=softcap, boost_radius=boost_radius, boost_factor=boost_factor, block_mask=block_mask)
+    return _attention_fn().apply(q, k, v, rel_bias, opts)
