@@ -87,7 +87,9 @@ typedef enum {
 } fa_mod_kind;
 
 typedef struct {
-  int32_t window;          /* FA_MASK_SLIDING_WINDOW: keys per query, >= 1 */
+  int32_t window;          /* FA_MASK_SLIDING_WINDOW: keys per query, >= 1
+                              (any value up to INT32_MAX; from max(Sq, Skv)
+                              on, the causal mask) */
   const int32_t* doc_ids;  /* FA_MASK_DOCUMENT: device int32 [B][S] */
   int32_t* visited;        /* optional debug output, device int32
                               [B][Hq][ceil(Sq/128)]: fa_fwd ADDS the number of

@@ -248,6 +248,25 @@ def test_fused_row_pass_same_bits(case):
     assert not torch.isnan(ref_rows[1]).any()
 
 
+@pytest.mark.parametrize("Sq,Skv", [(700, 700), (333, 500), (1500, 1500)])
+def test_huge_window_is_causal(Sq, Skv):
+    """A window of 2^31 - 1 keys admits exactly the causal pairs: forward and
+    backward give the causal mask's bits (the host clamps the window to
+    max(Sq, Skv), so no kernel's range arithmetic overflows)."""
+    B, Hq, Hkv, D = 1, 4, 2, 128
+    q, _, _ = synth.qkv(B, Hq, Hkv, Sq, Sq, D, 60 + Sq)
+    _, k, v = synth.qkv(B, Hq, Hkv, Skv, Skv, D, 61 + Skv)
+    q, k, v = dev(q), dev(k), dev(v)
+    do = dev(synth.randn((B, Hq, Sq, D), 62))
+    res = []
+    for spec in (dict(mask=fa.MASK_CAUSAL), dict(mask=fa.MASK_SLIDING_WINDOW, window=2**31 - 1)):
+        o, lse = fa.forward(q, k, v, return_lse=True, **spec)
+        res.append((o, lse, *fa.backward(q, k, v, o, do, lse, **spec)))
+    torch.cuda.synchronize()
+    for a, b, what in zip(res[0], res[1], ("O", "LSE", "dQ", "dK", "dV")):
+        assert torch.equal(a, b), what
+
+
 @pytest.mark.parametrize("B,Hq,Hkv,S", [(2, 8, 4, 700), (4, 8, 2, 200)])
 def test_xcd_pinned_schedule(B, Hq, Hkv, S):
     """dQ and dK/dV under the XCD-pinned schedule (B * Hkv a multiple of 8),

@@ -54,7 +54,10 @@ int check_variant(int B, int Hq, int Sq, int Skv, float scale, int mask_kind, co
     case FA_MASK_SLIDING_WINDOW:
       if (!mp) return FA_ERR_NULL;
       if (mp->window < 1) return FA_ERR_PARAM;
-      mask.window = mp->window;
+      // Every admissible pair has i - j < max(Sq, Skv), so a larger window
+      // admits the same pairs; the clamp keeps the kernels' range arithmetic
+      // (first key + tile + window) far from int overflow.
+      mask.window = (int)std::min<long long>(mp->window, std::max<long long>(std::max(Sq, Skv), 1));
       break;
     case FA_MASK_DOCUMENT:
       if (!mp || !mp->doc_ids) return FA_ERR_NULL;
