@@ -17,6 +17,9 @@ Readings where the pages are silent (listed in the design notes):
     mantissa bits, no infinities, NaN = S.1111.111, largest finite 448,
     subnormals m/8 * 2^-6), rounding to nearest, ties to even, saturating
     at +-448.
+  * Non-finite inputs: quantization is elementwise, so a NaN stays NaN (its
+    code 0x7F with the sign bit) and +-Inf saturates at +-448 like any value
+    out of range; a block's scale comes from its finite values.
   * The random orthogonal matrix is M = diag(s) H_D / sqrt(D): H_D the
     Sylvester Hadamard matrix, s a seeded vector of random signs; rows are
     transformed as x M.  V is not transformed (it is not part of Q K^T).
@@ -71,9 +74,11 @@ def e4m3_decode(codes) -> np.ndarray:
 
 def e4m3_encode(x) -> np.ndarray:
     """Round to the nearest E4M3 value, ties to the even code; saturate at
-    +-448."""
+    +-448 (infinities included); NaN gives the NaN code 0x7F (sign bit of
+    the input kept)."""
     x = np.asarray(x, dtype=np.float64)
-    a = np.minimum(np.abs(x), E4M3_MAX)
+    nan = np.isnan(x)
+    a = np.minimum(np.abs(np.where(nan, 0.0, x)), E4M3_MAX)
     hi = np.searchsorted(_POS, a, side="left")          # first value >= a
     hi = np.minimum(hi, len(_POS) - 1)
     lo = np.maximum(hi - 1, 0)
@@ -81,6 +86,7 @@ def e4m3_encode(x) -> np.ndarray:
     d_lo, d_hi = a - _POS[lo], _POS[hi] - a
     take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
     code = np.where(exact, hi, np.where(take_hi, hi, lo)).astype(np.uint8)
+    code = np.where(nan, 0x7F, code).astype(np.uint8)
     return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
 
 
@@ -125,7 +131,8 @@ def block_quantize(x, signs=None, block: int = QBLOCK):
     for r in range(R):
         for b in range(nb):
             blk = y[r, b * block:(b + 1) * block]
-            e = block_scale_exponent(float(np.abs(blk).max()) if blk.size else 0.0)
+            fin = np.abs(blk[np.isfinite(blk)])  # the scale comes from the finite values
+            e = block_scale_exponent(float(fin.max()) if fin.size else 0.0)
             scales[r, b] = e + 127
             codes[r, b * block:(b + 1) * block] = e4m3_encode(blk * 2.0 ** -e)
     return codes, scales

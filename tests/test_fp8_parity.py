@@ -72,6 +72,40 @@ def test_quantize_matches_oracle(D, signed):
         assert a <= yv <= b and abs(yv - (a + b) / 2) <= 1e-5 * abs(yv) + 1e-30, (r, i, d, yv, a, b)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_quantize_non_finite(D):
+    """NaN keeps a NaN code, infinities saturate to +-448, and the block scale
+    comes from the finite values, as in the oracle; with the incoherence
+    transform a NaN spreads over its row only."""
+    B, H, S = 1, 2, 200
+    x = synth.randn((B, H, S, D), 73, "f32")
+    x[0, 0, 5, 3], x[0, 0, 9, 4], x[0, 1, 150, 0] = float("nan"), float("inf"), float("-inf")
+    x = x.to(torch.bfloat16)
+    x8, sc = fa.quantize_fp8(x.cuda())
+    torch.cuda.synchronize()
+    codes, scales = ofp8.block_quantize(_f64(x).reshape(B * H, S, D))
+    got = x8.cpu().numpy().reshape(B * H, S, D)
+    assert np.array_equal(sc.cpu().numpy().reshape(B * H, -1), scales)
+    assert got[0, 5, 3] & 0x7F == 0x7F and got[0, 9, 4] == 0x7E and got[1, 150, 0] == 0xFE
+    keep = np.ones(got.shape, bool)
+    keep[0, 5, 3] = keep[0, 9, 4] = keep[1, 150, 0] = False
+    assert np.count_nonzero(got[keep] != codes[keep]) <= 3
+    # Incoherence transform: the NaN row becomes NaN codes; no other row changes.
+    s = synth.signs(D, 74)
+    y = x.clone()
+    y[0, 0, 9, 4] = 1.0
+    y[0, 1, 150, 0] = -1.0
+    y8, ysc = fa.quantize_fp8(y.cuda(), s.cuda())
+    torch.cuda.synchronize()
+    ycodes, yscales = ofp8.block_quantize(_f64(y).reshape(B * H, S, D), s.numpy())
+    yg = y8.cpu().numpy().reshape(B * H, S, D)
+    assert np.array_equal(ysc.cpu().numpy().reshape(B * H, -1), yscales)
+    assert np.all(yg[0, 5] & 0x7F == 0x7F) and np.all(ycodes[0, 5] & 0x7F == 0x7F)
+    rest = np.ones(yg.shape, bool)
+    rest[0, 5] = False
+    assert np.count_nonzero(yg[rest] != ycodes[rest]) <= max(3, yg.size // 10000)
+
+
 def _oracle_quantized(B, Hq, Hkv, S, D, seed, signs):
     q, k, v = synth.qkv(B, Hq, Hkv, S, S, D, seed)
     s = signs.numpy()

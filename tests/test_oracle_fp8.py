@@ -42,6 +42,24 @@ def test_e4m3_ties_to_even_and_saturation():
     assert enc(-0.0) == 0x80
 
 
+def test_non_finite_inputs():
+    """NaN keeps its NaN code (0x7F, sign bit kept), infinities saturate, and
+    a block's scale ignores them: the finite values quantize as they would
+    alone."""
+    codes = fp8.e4m3_encode(np.array([np.nan, -np.nan, np.inf, -np.inf]))
+    assert codes[0] == 0x7F and codes[1] == 0xFF and codes[2] == 0x7E and codes[3] == 0xFE
+    x = np.linspace(-3.0, 5.0, 4 * 64).reshape(1, 4, 64)
+    c_ref, s_ref = fp8.block_quantize(x)
+    y = x.copy()
+    y[0, 1, 3], y[0, 2, 7], y[0, 3, 9] = np.nan, np.inf, -np.inf
+    c, s = fp8.block_quantize(y)
+    assert np.array_equal(s, s_ref)
+    assert c[0, 1, 3] == 0x7F and c[0, 2, 7] == 0x7E and c[0, 3, 9] == 0xFE
+    keep = np.ones(c.shape, bool)
+    keep[0, 1, 3] = keep[0, 2, 7] = keep[0, 3, 9] = False
+    assert np.array_equal(c[keep], c_ref[keep])
+
+
 def test_e4m3_encode_is_nearest_value():
     """Brute force over the value table: the nearest finite value, ties to
     the even code."""

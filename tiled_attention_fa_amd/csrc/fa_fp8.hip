@@ -111,9 +111,11 @@ __global__ __launch_bounds__(128) void fp8_quantize_kernel(const uint16_t* __res
 #pragma unroll
     for (int d = 0; d < D; ++d) v[d] *= rs;
   }
+  // The block scale comes from the finite values; a NaN stays NaN (E4M3's
+  // NaN code) and +-Inf saturates at +-448 like any value out of range.
   float amax = 0.0f;
 #pragma unroll
-  for (int d = 0; d < D; ++d) amax = fmaxf(amax, fabsf(v[d]));
+  for (int d = 0; d < D; ++d) amax = fmaxf(amax, __builtin_isfinite(v[d]) ? fabsf(v[d]) : 0.0f);
   __shared__ float s_max[2];
   for (int w = 32; w >= 1; w >>= 1) amax = fmaxf(amax, __shfl_xor(amax, w));
   if ((t & 63) == 0) s_max[t >> 6] = amax;
@@ -138,7 +140,10 @@ __global__ __launch_bounds__(128) void fp8_quantize_kernel(const uint16_t* __res
       for (int k = 0; k < 4; ++k) {
         float f[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f[i] = fminf(fmaxf(ldexpf(v[16 * c + 4 * k + i], -e), -448.0f), 448.0f);
+        for (int i = 0; i < 4; ++i) {
+          const float y = ldexpf(v[16 * c + 4 * k + i], -e);
+          f[i] = y != y ? y : fminf(fmaxf(y, -448.0f), 448.0f);
+        }
         const int lo = pack_fp8<false>(f[0], f[1], 0);
         w[k] = (uint32_t)pack_fp8<true>(f[2], f[3], lo);
       }
